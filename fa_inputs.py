@@ -1,0 +1,113 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module draws random numbers and rounds them to the storage formats the
+attention path consumes. It holds none of the attention arithmetic: no score,
+softmax, quantisation or rotation is computed here. Both the GPU path and the
+CPU oracle receive exactly the arrays produced here.
+
+Workloads (all synthetic; the pages measure on synthetic data themselves):
+  * iid N(0,1) entries for Q, K, V, rounded to bf16 with round-to-nearest-even
+    (the attention benchmark of the QbitAI FlashAttention-3 article, section on
+    the attention benchmark, sweeps sequence length at 16k total tokens with
+    random inputs).
+  * the outlier model of that article's FP8 accuracy test: N(0,1) entries of
+    which a fraction 0.001 carry a large N(0, 10^2) component. Two readings are
+    provided: "replace" (the outlier value replaces the entry) and "add" (the
+    outlier value is added to the entry, as that article words it).
+  * random signs in {-1, +1} for the random-sign Hadamard rotation used by
+    incoherent processing (FlashAttention-3 (HE), section on FP8 with
+    incoherent processing).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16, round-to-nearest-even; return the
+    16-bit patterns as uint16 (same layout as torch.bfloat16)."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact upcast of bfloat16 bit patterns to float64."""
+    u = bits.astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def draw(rng: np.random.Generator, shape, dist: str = "normal",
+         outlier_p: float = 0.001, outlier_sd: float = 10.0) -> np.ndarray:
+    """Draw one float32 tensor of the given distribution."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if dist == "normal":
+        return x
+    mask = rng.random(shape) < outlier_p
+    big = (rng.standard_normal(shape, dtype=np.float32) * np.float32(outlier_sd))
+    if dist == "outlier_replace":
+        return np.where(mask, big, x).astype(np.float32)
+    if dist == "outlier_add":
+        return (x + np.where(mask, big, np.float32(0))).astype(np.float32)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+class QKV:
+    """Q, K, V of shape [B, H, N, d]: bf16 bit patterns plus exact float64."""
+
+    def __init__(self, B, H, N, d, seed, dist="normal"):
+        self.shape = (B, H, N, d)
+        self.seed = seed
+        self.dist = dist
+        rng = np.random.default_rng(seed)
+        self.q_bits = bf16_bits(draw(rng, self.shape, dist))
+        self.k_bits = bf16_bits(draw(rng, self.shape, dist))
+        self.v_bits = bf16_bits(draw(rng, self.shape, dist))
+
+    @property
+    def q(self):
+        return bf16_bits_to_f64(self.q_bits)
+
+    @property
+    def k(self):
+        return bf16_bits_to_f64(self.k_bits)
+
+    @property
+    def v(self):
+        return bf16_bits_to_f64(self.v_bits)
+
+
+def make_qkv(B, H, N, d, seed, dist="normal") -> QKV:
+    return QKV(B, H, N, d, seed, dist)
+
+
+def random_signs(d: int, seed: int) -> np.ndarray:
+    """d independent signs in {-1, +1} as float32."""
+    rng = np.random.default_rng(seed)
+    return np.where(rng.random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+
+
+def to_torch_bf16(bits: np.ndarray, device="cpu"):
+    """View uint16 bf16 patterns as a torch.bfloat16 tensor (no rounding)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def bf16_tensor_to_bits(t) -> np.ndarray:
+    """Inverse of to_torch_bf16: torch.bfloat16 tensor -> uint16 patterns."""
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# Seeds are fixed per workload in advance.
+SEEDS = {
+    "small": 1,          # B=1 H=2 N=256 d=64
+    "mid": 2,            # B=4 H=16 N=2048 d=128
+    "seq_sweep_base": 300,   # + log2(N/512)
+    "dim_sweep_base": 400,   # + index of d in (64, 96, 128, 256)
+    "fp8": 5,
+    "fp8_signs": 55,
+}

@@ -1,0 +1,23 @@
+"""The oracle: plain, slow, float64 CPU implementations of what the attention
+path computes, written from the pages' descriptions.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check of the entry module and
+the CPU-baseline leg of the benchmark may import, call or run anything in this
+package. The product path (the C-ABI library and its Python binding) never
+uses it and shares no code, table or helper with it.
+
+Contents
+  attention.py  exact softmax(scale * Q K^T) V and per-row log-sum-exp in
+                float64, materialising S and P (pinned: closed forms,
+                brute force, invariants, a library routine).
+  fp8.py        e4m3fn encode/decode, per-block and per-tensor quantisation
+                with optional random-sign Hadamard rotation (pinned: a library
+                cast, the format's closed forms, H H^T = d I, rotation
+                invariance of attention), and an FP8 attention emulator used
+                only to predict the FP8 kernel's error. The emulator's
+                prediction is "parity unpinned" beyond the reduction case
+                where its inputs are exactly representable (then it equals
+                exact attention up to the rounding of P).
+"""
+from .attention import attention, attention_rows, attention_sampled  # noqa: F401
+from . import fp8  # noqa: F401
