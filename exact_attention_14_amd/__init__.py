@@ -1,0 +1,161 @@
+"""Python binding of libfa.so, the MI355X FlashAttention forward library.
+
+Argument marshalling only: tensors are checked, outputs are allocated with
+torch on the caller's device, and the C entry points of include/fa.h are called
+on torch's current stream. Every step of the attention path runs in the
+library's HIP kernels; there is no fallback. Importing this package fails
+loudly when libfa.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_BF16 = 0
+FA_FP8_E4M3 = 1
+FP8_BLOCK = 128
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_MISALIGNED = -3
+FA_ERR_HIP = -4
+FA_ERR_TOO_LARGE = -5
+
+EXPORTS = ("fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_status_string", "fa_version")
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first with "
+            "`python -m exact_attention_14_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fp = ctypes.c_void_p
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_quant_fp8.argtypes = [vp, vp, fp, i, i, i, i, i, fp, vp]
+    lib.fa_quant_fp8.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.fa_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib.fa_version())
+
+
+def _check(status: int, fn: str):
+    if status != FA_OK:
+        raise FAError(status, fn)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_qkv(q, k, v, dtype):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v are on different devices")
+    return torch
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, dtype: int = FA_BF16,
+        out=None, lse=None, return_lse: bool = True):
+    """Attention forward on bf16 [B, H, N, d] tensors; returns (o, lse).
+
+    dtype=FA_BF16 runs the bf16 path; dtype=FA_FP8_E4M3 the end-to-end FP8
+    path (rotation, block quantisation and the e4m3 kernel inside the call).
+    """
+    torch = _check_qkv(q, k, v, torch_bf16())
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
+                    float(scale), int(dtype), _stream(q.device))
+    _check(st, "fa_fwd")
+    return o, lse
+
+
+def quant_fp8(x, per_tensor: bool = False, signs=None, out=None, scales=None):
+    """Block-quantise a bf16 [B, H, N, d] tensor to e4m3fn; returns (x8, scales)."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [B, H, N, d] tensor")
+    B, H, N, d = x.shape
+    nblk = (N + FP8_BLOCK - 1) // FP8_BLOCK
+    x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device) if out is None else out
+    sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device) if scales is None else scales
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d):
+        raise ValueError("signs must be a float32 tensor of d entries")
+    st = lib.fa_quant_fp8(_ptr(x), _ptr(x8), _ptr(sc), B, H, N, d, int(bool(per_tensor)),
+                          _ptr(signs), _stream(x.device))
+    _check(st, "fa_quant_fp8")
+    return x8, sc
+
+
+def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = None,
+            out=None, lse=None, return_lse: bool = True):
+    """Attention forward on e4m3fn operands with block scales; returns (o bf16, lse)."""
+    torch = _check_qkv(q8, k8, v8, _fp8())
+    B, H, N, d = q8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    st = lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv), _ptr(o),
+                        _ptr(lse), B, H, N, d, int(bool(causal)), float(scale),
+                        _stream(q8.device))
+    _check(st, "fa_fwd_fp8")
+    return o, lse
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
+
+
+def _fp8():
+    import torch
+    return torch.float8_e4m3fn

@@ -1,0 +1,157 @@
+// C-ABI entry points: host-side validation, dispatch and error mapping.
+// Every check runs before any HIP call, in the order the header states.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "../../include/fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr unsigned long long kSignKey = 0x5A17C0DEull;  // fixed rotation of FA_FP8_E4M3
+
+bool log_enabled() {
+  const char* e = std::getenv("FA_LOG");
+  return e != nullptr && e[0] == '1';
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool bf16_dim_ok(int d) { return d == 64 || d == 96 || d == 128 || d == 256; }
+bool fp8_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+bool pow2(int d) { return d > 0 && (d & (d - 1)) == 0; }
+
+int sizes_check(int B, int H, int N, int d) {
+  if ((long long)N * d >= (1LL << 31)) return FA_ERR_TOO_LARGE;
+  if ((long long)B * H >= (1LL << 31)) return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FA_OK;
+  if (log_enabled()) std::fprintf(stderr, "[fa] %s: %s\n", what, hipGetErrorString(e));
+  return FA_ERR_HIP;
+}
+
+int check_common(const void* q, const void* k, const void* v, void* o, int B, int H, int N) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int run_fp8_path(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int H, int N, int d, int causal, float scale, hipStream_t stream) {
+  // Stream-ordered scratch: three e4m3 tensors, three scale arrays, the signs.
+  const size_t elems = (size_t)B * H * N * d;
+  const size_t nblk = (size_t)B * H * ((N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK);
+  const size_t t_bytes = (elems + 255) & ~(size_t)255;
+  const size_t s_bytes = (nblk * sizeof(float) + 255) & ~(size_t)255;
+  const size_t total = 3 * t_bytes + 3 * s_bytes + 256 + d * sizeof(float);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, total, stream);
+  if (e != hipSuccess) return hip_status(e, "hipMallocAsync");
+  char* base = static_cast<char*>(ws);
+  void* q8 = base;
+  void* k8 = base + t_bytes;
+  void* v8 = base + 2 * t_bytes;
+  float* sq = reinterpret_cast<float*>(base + 3 * t_bytes);
+  float* sk = reinterpret_cast<float*>(base + 3 * t_bytes + s_bytes);
+  float* sv = reinterpret_cast<float*>(base + 3 * t_bytes + 2 * s_bytes);
+  float* signs = reinterpret_cast<float*>(base + 3 * t_bytes + 3 * s_bytes);
+  e = fa::launch_fill_signs(signs, d, kSignKey, stream);
+  if (e == hipSuccess) e = fa::launch_quant_fp8(q, q8, sq, B, H, N, d, false, signs, stream);
+  if (e == hipSuccess) e = fa::launch_quant_fp8(k, k8, sk, B, H, N, d, false, signs, stream);
+  if (e == hipSuccess) e = fa::launch_quant_fp8(v, v8, sv, B, H, N, d, false, nullptr, stream);
+  if (e == hipSuccess)
+    e = fa::launch_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse, B, H, N, d, causal != 0, scale,
+                           stream);
+  hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return hip_status(e, "fp8 path launch");
+  return hip_status(ef, "hipFreeAsync");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int d, int causal, float scale, int dtype, void* stream) {
+  int st = check_common(q, k, v, o, B, H, N);
+  if (st != FA_OK) return st;
+  if (dtype == FA_BF16) {
+    if (!bf16_dim_ok(d)) return FA_ERR_UNSUPPORTED;
+  } else if (dtype == FA_FP8_E4M3) {
+    if (!fp8_dim_ok(d) || !pow2(d)) return FA_ERR_UNSUPPORTED;
+  } else {
+    return FA_ERR_UNSUPPORTED;
+  }
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  st = sizes_check(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse != nullptr && !aligned16(lse)))
+    return FA_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (log_enabled())
+    std::fprintf(stderr, "[fa] fa_fwd dtype=%d B=%d H=%d N=%d d=%d causal=%d scale=%g\n", dtype,
+                 B, H, N, d, causal, (double)scale);
+  if (dtype == FA_BF16)
+    return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal != 0, scale, s),
+                      "fwd_bf16 launch");
+  return run_fp8_path(q, k, v, o, lse, B, H, N, d, causal, scale, s);
+}
+
+int fa_quant_fp8(const void* x, void* x8, float* scales, int B, int H, int N, int d,
+                 int per_tensor, const float* signs, void* stream) {
+  if (x == nullptr || x8 == nullptr || scales == nullptr) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (!bf16_dim_ok(d) || (signs != nullptr && !pow2(d))) return FA_ERR_UNSUPPORTED;
+  int st = sizes_check(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(scales) ||
+      (signs != nullptr && !aligned16(signs)))
+    return FA_ERR_MISALIGNED;
+  return hip_status(fa::launch_quant_fp8(x, x8, scales, B, H, N, d, per_tensor != 0, signs,
+                                         static_cast<hipStream_t>(stream)),
+                    "quant_fp8 launch");
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
+               const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
+               int N, int d, int causal, float scale, void* stream) {
+  int st = check_common(q8, k8, v8, o, B, H, N);
+  if (st != FA_OK) return st;
+  if (q_scale == nullptr || k_scale == nullptr || v_scale == nullptr) return FA_ERR_INVALID_ARG;
+  if (!fp8_dim_ok(d)) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  st = sizes_check(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) ||
+      !aligned16(q_scale) || !aligned16(k_scale) || !aligned16(v_scale) ||
+      (lse != nullptr && !aligned16(lse)))
+    return FA_ERR_MISALIGNED;
+  return hip_status(fa::launch_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N,
+                                       d, causal != 0, scale, static_cast<hipStream_t>(stream)),
+                    "fwd_fp8 launch");
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
+    case FA_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
+    case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_TOO_LARGE: return "size beyond 32-bit index limits";
+    default: return "unknown status";
+  }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// Host-side launchers of the attention kernels. Arguments are validated by the
+// C-ABI layer (fa_api.cpp) before these are called.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+// bf16 forward: d in {64, 96, 128, 256}.
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
+                           float* lse, int B, int H, int N, int d, bool causal,
+                           float scale, hipStream_t stream);
+
+// Block quantisation of one bf16 tensor to e4m3fn.
+hipError_t launch_quant_fp8(const void* x, void* x8, float* scales, int B, int H,
+                            int N, int d, bool per_tensor, const float* signs,
+                            hipStream_t stream);
+
+// FP8 forward: d in {64, 128, 256}.
+hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                          const float* sq, const float* sk, const float* sv,
+                          void* o, float* lse, int B, int H, int N, int d,
+                          bool causal, float scale, hipStream_t stream);
+
+// Writes d random signs (+-1) derived from a fixed 64-bit key.
+hipError_t launch_fill_signs(float* signs, int d, unsigned long long key,
+                             hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,137 @@
+/*
+ * fa.h - FlashAttention forward for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The library computes exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T) V,   LSE_i = log sum_j exp(scale * q_i . k_j)
+ * without ever materialising the N x N score matrix: Q, K and V are tiled
+ * through on-chip memory and the softmax is taken online, with a running row
+ * maximum and row sum and a rescaling of the output accumulator (droidorbit
+ * FlashAttention-3 explainer, "Mathematical Formulation: The Online Softmax
+ * Rescaling Trick"; dibro.site FlashAttention-3 post, "Arquitectura y
+ * metodo"). Causal attention skips key tiles that lie wholly after every
+ * query of a query tile (dibro.site post, "Contribuciones clave").
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are contiguous row-major [B, H, N, d]: element (b, h, n, i) is
+ *     at offset ((b*H + h)*N + n)*d + i. Q, K, V and O share one N
+ *     (self-attention lengths) and one d.
+ *   - bf16 tensors hold the bit patterns of bfloat16 (torch.bfloat16).
+ *     fp8 tensors hold OCP e4m3fn bytes (torch.float8_e4m3fn).
+ *   - LSE is float32 [B, H, N], the natural log of sum_j exp(scale*q_i.k_j)
+ *     over the keys row i attends. It may be NULL to skip its store.
+ *   - Causal (causal != 0): query i attends key j only when j <= i.
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned. The library never frees or keeps them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work and return; the caller keeps buffers alive
+ *     until the stream has completed them. Faults inside a kernel surface at
+ *     the caller's next synchronisation, not in the return code.
+ *   - Arguments are validated on the host before any HIP call, in the order
+ *     listed for each function. No C++ exception crosses this boundary.
+ *     Nothing is printed unless the environment variable FA_LOG=1 is set.
+ *   - Thread-safe and re-entrant: the library holds no mutable global state.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_dtype {
+    FA_BF16 = 0,      /* bf16 Q/K/V in, bf16 O out                                */
+    FA_FP8_E4M3 = 1   /* bf16 Q/K/V in, quantised to e4m3 inside the call, bf16 O  */
+} fa_dtype;
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, bad scale     */
+    FA_ERR_UNSUPPORTED = -2,   /* head dimension or dtype not instantiated       */
+    FA_ERR_MISALIGNED = -3,    /* a tensor pointer is not 16-byte aligned        */
+    FA_ERR_HIP = -4,           /* the HIP runtime reported an error at launch    */
+    FA_ERR_TOO_LARGE = -5      /* N*d or B*H beyond the 32-bit index limits      */
+} fa_status;
+
+/* Rows per FP8 quantisation block: one fp32 scale per 128 consecutive
+ * sequence rows of one (batch, head), all d columns. */
+#define FA_FP8_BLOCK 128
+
+/*
+ * fa_fwd - attention forward pass.
+ *
+ * q, k, v : bf16 [B, H, N, d] (inputs)       o : bf16 [B, H, N, d] (output)
+ * lse     : float32 [B, H, N] or NULL         scale : softmax scale, finite > 0
+ *           (callers normally pass 1/sqrt(d), the equation's scaling)
+ * d       : 64, 96, 128 or 256 for FA_BF16; 64, 128 or 256 for FA_FP8_E4M3
+ * dtype   : FA_BF16 runs the bf16 matrix-core path.
+ *           FA_FP8_E4M3 runs the FP8 path end to end on bf16 inputs: Q and K
+ *           are rotated by a fixed random-sign Hadamard matrix and all three
+ *           are block-quantised to e4m3 (fa_quant_fp8) into stream-ordered
+ *           scratch (hipMallocAsync/hipFreeAsync on `stream`), then
+ *           fa_fwd_fp8 runs. d must be a power of two.
+ * Validation order: null q/k/v/o -> INVALID_ARG; B, H or N < 1 -> INVALID_ARG;
+ * dtype unknown or d unsupported -> UNSUPPORTED; scale not finite and > 0 ->
+ * INVALID_ARG; N*d >= 2^31 or B*H >= 2^31 -> TOO_LARGE; a pointer not 16-byte
+ * aligned -> MISALIGNED; launch (or scratch allocation) error -> HIP.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, int causal, float scale, int dtype,
+           void* stream);
+
+/*
+ * fa_quant_fp8 - block quantisation of one bf16 tensor to e4m3fn
+ * (QbitAI FlashAttention-3 article, FP8 section: block-wise quantisation and
+ * incoherent processing; FlashAttention-3 (HE), FP8 with reduced
+ * quantisation error: rotation by a random orthogonal Hadamard matrix).
+ *
+ * x      : bf16 [B, H, N, d] (input)       x8 : e4m3fn [B, H, N, d] (output)
+ * scales : float32 [B, H, ceil(N/128)] (output): dequantised value of an
+ *          element = e4m3 value * scales[b, h, n/128].
+ * per_tensor : 0 = one scale per 128-row block; 1 = one scale for the whole
+ *          tensor, written to every entry of `scales`.
+ * signs  : NULL (no rotation) or float32 [d] of +-1 on the device: x is
+ *          rotated to x diag(signs) H_d / sqrt(d), H_d the Sylvester Hadamard
+ *          matrix (d a power of two). Rotate Q and K with the same signs,
+ *          never V.
+ * Quantisation: y = x diag(signs) H_d (float32; y = x without rotation),
+ * s = amax|y| / 448 over the block (float32; 1 for an all-zero block),
+ * code = round-to-nearest-even e4m3(clamp(y / s, +-448)); the stored scale is
+ * s, or s * (1/sqrt(d)) with rotation.
+ * Validation order: null x/x8/scales -> INVALID_ARG; B, H or N < 1 ->
+ * INVALID_ARG; d not in {64, 96, 128, 256}, or signs given and d not a power
+ * of two -> UNSUPPORTED; size limits -> TOO_LARGE; misaligned -> MISALIGNED;
+ * launch error -> HIP.
+ */
+int fa_quant_fp8(const void* x, void* x8, float* scales,
+                 int B, int H, int N, int d, int per_tensor, const float* signs,
+                 void* stream);
+
+/*
+ * fa_fwd_fp8 - attention forward pass on e4m3 operands with float32
+ * accumulation and an fp32 online softmax (QbitAI article, FP8 section;
+ * vikram-blog FlashAttention-3 post, "Production Gotchas": softmax state
+ * stays in FP32).
+ *
+ * q8, k8, v8 : e4m3fn [B, H, N, d] with block scales q_scale, k_scale,
+ *              v_scale : float32 [B, H, ceil(N/128)] as fa_quant_fp8 writes.
+ * o : bf16 [B, H, N, d]; lse : float32 [B, H, N] or NULL; d : 64, 128, 256.
+ * The probabilities P are multiplied by 256 and rounded to e4m3 for the P V
+ * product; the row sum uses the unrounded float32 P.
+ * Validation order as fa_fwd (null scale arrays -> INVALID_ARG).
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
+               const float* q_scale, const float* k_scale, const float* v_scale,
+               void* o, float* lse, int B, int H, int N, int d, int causal,
+               float scale, void* stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* fa_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

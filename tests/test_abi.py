@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every symbol include/fa.h declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(fa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_expected_api():
+    assert declared_functions() == sorted(
+        ["fa_fwd", "fa_fwd_fp8", "fa_quant_fp8", "fa_status_string", "fa_version"])
+
+
+def test_library_exports_all_declared(lib):
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(lib.EXPORTS) == set(declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.version() >= 100
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.status_string(st) and lib.status_string(st) != "unknown status"
+    assert lib.status_string(12345) == "unknown status"
+
+
+P = 4096  # a 16-byte-aligned fake address; never dereferenced (validation fails first)
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=None, B=1, H=1, N=8, d=64, causal=0, scale=0.125,
+        dtype=0):
+    return lib.lib.fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, None)
+
+
+def test_fwd_validation_order(lib):
+    assert fwd(lib, q=None) == lib.FA_ERR_INVALID_ARG
+    assert fwd(lib, o=None) == lib.FA_ERR_INVALID_ARG
+    assert fwd(lib, B=0) == lib.FA_ERR_INVALID_ARG
+    assert fwd(lib, N=-3) == lib.FA_ERR_INVALID_ARG
+    assert fwd(lib, d=80) == lib.FA_ERR_UNSUPPORTED
+    assert fwd(lib, dtype=7) == lib.FA_ERR_UNSUPPORTED
+    assert fwd(lib, d=96, dtype=lib.FA_FP8_E4M3) == lib.FA_ERR_UNSUPPORTED
+    assert fwd(lib, scale=0.0) == lib.FA_ERR_INVALID_ARG
+    assert fwd(lib, scale=float("nan")) == lib.FA_ERR_INVALID_ARG
+    assert fwd(lib, scale=float("inf")) == lib.FA_ERR_INVALID_ARG
+    assert fwd(lib, N=1 << 25, d=64) == lib.FA_ERR_TOO_LARGE
+    assert fwd(lib, q=P + 2) == lib.FA_ERR_MISALIGNED
+    assert fwd(lib, lse=P + 4) == lib.FA_ERR_MISALIGNED
+    # earlier checks win over later ones
+    assert fwd(lib, q=None, d=80) == lib.FA_ERR_INVALID_ARG
+    assert fwd(lib, d=80, scale=-1.0) == lib.FA_ERR_UNSUPPORTED
+    assert fwd(lib, scale=-1.0, q=P + 2) == lib.FA_ERR_INVALID_ARG
+
+
+def test_quant_validation(lib):
+    q = lib.lib.fa_quant_fp8
+    assert q(None, P, P, 1, 1, 8, 64, 0, None, None) == lib.FA_ERR_INVALID_ARG
+    assert q(P, P, None, 1, 1, 8, 64, 0, None, None) == lib.FA_ERR_INVALID_ARG
+    assert q(P, P, P, 1, 0, 8, 64, 0, None, None) == lib.FA_ERR_INVALID_ARG
+    assert q(P, P, P, 1, 1, 8, 72, 0, None, None) == lib.FA_ERR_UNSUPPORTED
+    assert q(P, P, P, 1, 1, 8, 96, 0, P, None) == lib.FA_ERR_UNSUPPORTED   # rotation needs 2^k
+    assert q(P, P + 8, P, 1, 1, 8, 64, 0, None, None) == lib.FA_ERR_MISALIGNED
+
+
+def test_fwd_fp8_validation(lib):
+    f = lib.lib.fa_fwd_fp8
+    args = dict(q8=P, k8=P, v8=P, sq=P, sk=P, sv=P, o=P, lse=None, B=1, H=1, N=8, d=128,
+                causal=0, scale=0.1)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q8"], a["k8"], a["v8"], a["sq"], a["sk"], a["sv"], a["o"], a["lse"], a["B"],
+                 a["H"], a["N"], a["d"], a["causal"], a["scale"], None)
+
+    assert call(v8=None) == lib.FA_ERR_INVALID_ARG
+    assert call(sk=None) == lib.FA_ERR_INVALID_ARG
+    assert call(H=0) == lib.FA_ERR_INVALID_ARG
+    assert call(d=96) == lib.FA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == lib.FA_ERR_INVALID_ARG
+    assert call(sv=P + 4) == lib.FA_ERR_MISALIGNED
+
+
+def test_python_wrapper_rejects_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lib.fwd(x, x, x)
+    with pytest.raises(TypeError):
+        lib.fwd(x.float(), x, x)

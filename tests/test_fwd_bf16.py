@@ -1,0 +1,152 @@
+"""GPU parity of the bf16 forward pass against the float64 oracle.
+
+Every case prints its name, shape and seed before it touches the GPU.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import fa_inputs
+from oracle import attention, attention_sampled
+from tests.gpu_util import (LSE_MAX_ABS, bf16_gate, run_bf16, sample_rows, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(*args):
+    print("[case]", *args, file=sys.stderr, flush=True)
+
+
+def check_full(fa, B, H, N, d, causal, seed, dist="normal"):
+    announce("full", B, H, N, d, "causal" if causal else "noncausal", "seed", seed)
+    g = fa_inputs.make_qkv(B, H, N, d, seed, dist)
+    o_gpu, lse_gpu = run_bf16(fa, g, causal)
+    o_ref, lse_ref = attention(g.q, g.k, g.v, causal)
+    ok, st = bf16_gate(o_gpu, o_ref)
+    lse_err = float(np.abs(lse_gpu - lse_ref).max())
+    announce("  stats", st, "lse_max_abs", lse_err)
+    assert ok, st
+    assert lse_err <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_config(lib, causal):
+    check_full(lib, 1, 2, 256, 64, causal, fa_inputs.SEEDS["small"])
+
+
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 65, 127, 129, 300])
+def test_ragged_lengths(lib, N, d):
+    for causal in (False, True):
+        check_full(lib, 1, 2, N, d, causal, 7000 + N + d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mid_config_full(lib, causal):
+    check_full(lib, 4, 16, 2048, 128, causal, fa_inputs.SEEDS["mid"])
+
+
+def check_sampled(fa, B, H, N, d, causal, seed, nsamples=96):
+    announce("sampled", B, H, N, d, "causal" if causal else "noncausal", "seed", seed)
+    g = fa_inputs.make_qkv(B, H, N, d, seed)
+    o_gpu, lse_gpu = run_bf16(fa, g, causal)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu))
+    rows = sample_rows(B, H, N, nsamples, seed)
+    o_ref, lse_ref = attention_sampled(g.q, g.k, g.v, rows, causal)
+    o_s = o_gpu[rows[:, 0], rows[:, 1], rows[:, 2]]
+    l_s = lse_gpu[rows[:, 0], rows[:, 1], rows[:, 2]]
+    ok, st = bf16_gate(o_s, o_ref)
+    lse_err = float(np.abs(l_s - lse_ref).max())
+    announce("  stats", st, "lse_max_abs", lse_err)
+    assert ok, st
+    assert lse_err <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("N", [512, 1024, 2048, 4096, 8192, 16384])
+def test_sequence_sweep_sampled(lib, N):
+    seed = fa_inputs.SEEDS["seq_sweep_base"] + int(math.log2(N // 512))
+    for causal in (False, True):
+        check_sampled(lib, 16384 // N, 16, N, 128, causal, seed)
+
+
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
+def test_head_dim_sweep_sampled(lib, d):
+    seed = fa_inputs.SEEDS["dim_sweep_base"] + (64, 96, 128, 256).index(d)
+    check_sampled(lib, 2, 16, 8192, d, True, seed)
+
+
+def test_closed_form_identical_keys(lib):
+    import torch
+    announce("closed-form identical keys")
+    B, H, N, d = 1, 2, 333, 128
+    g = fa_inputs.make_qkv(B, H, N, d, 11)
+    g.k_bits = np.broadcast_to(g.k_bits[:, :, :1, :], g.k_bits.shape).copy()
+    for causal in (False, True):
+        o_gpu, _ = run_bf16(lib, g, causal)
+        v = g.v
+        if causal:
+            expect = np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+        else:
+            expect = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+        ok, st = bf16_gate(o_gpu, expect)
+        assert ok, st
+
+
+def test_closed_form_causal_row0_bit_exact(lib):
+    announce("closed-form causal row 0")
+    g = fa_inputs.make_qkv(2, 3, 500, 128, 12)
+    o_gpu, lse_gpu = run_bf16(lib, g, True)
+    np.testing.assert_array_equal(o_gpu[:, :, 0], g.v[:, :, 0])
+    lse0 = np.einsum("bhd,bhd->bh", g.q[:, :, 0], g.k[:, :, 0]) / math.sqrt(128)
+    np.testing.assert_allclose(lse_gpu[:, :, 0], lse0, rtol=0, atol=1e-4)
+
+
+def test_closed_form_one_hot_huge_scale(lib):
+    announce("closed-form one-hot query, scale 1e4")
+    B, H, N, d = 1, 1, 300, 64
+    g = fa_inputs.make_qkv(B, H, N, d, 13)
+    cols = np.arange(N) % d
+    qv = np.zeros((N, d), dtype=np.float32)
+    qv[np.arange(N), cols] = 1.0
+    g.q_bits = fa_inputs.bf16_bits(qv)[None, None]
+    k = g.k[0, 0]
+    for causal in (False, True):
+        o_gpu, _ = run_bf16(lib, g, causal, scale=1e4)
+        for i in range(N):
+            keys = np.arange(i + 1) if causal else np.arange(N)
+            col = k[keys, cols[i]]
+            srt = np.sort(col)
+            if len(col) > 1 and srt[-1] == srt[-2]:
+                continue  # tie: the selected row is not unique
+            j = keys[np.argmax(col)]
+            np.testing.assert_array_equal(o_gpu[0, 0, i], g.v[0, 0, j])
+
+
+def test_deterministic(lib):
+    import torch
+    announce("determinism")
+    g = fa_inputs.make_qkv(2, 4, 1000, 128, 14)
+    q, k, v = to_device(g)
+    o1, l1 = lib.fwd(q, k, v, causal=True)
+    o2, l2 = lib.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_lse_optional_and_scale(lib):
+    import torch
+    announce("lse NULL and explicit scale")
+    g = fa_inputs.make_qkv(1, 2, 200, 64, 15)
+    q, k, v = to_device(g)
+    o, lse = lib.fwd(q, k, v, causal=False, scale=0.05, return_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    o_ref, _ = attention(g.q, g.k, g.v, False, 0.05)
+    o_gpu = fa_inputs.bf16_bits_to_f64(fa_inputs.bf16_tensor_to_bits(o))
+    ok, st = bf16_gate(o_gpu, o_ref)
+    assert ok, st
