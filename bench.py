@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Attention forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+
+One step is one fa_fwd call (bf16, non-causal) over the workload
+B=4, H=16, N=2048, d=128 with inputs resident in HBM. The metric is attention
+TFLOP/s = 4*B*H*N^2*d / time (halved for causal masks). Rank 0 prints one JSON
+line. The extra measurements (causal, the sequence and head-dimension sweeps,
+the FP8 path) ride along in "extra"; the CPU baseline times the float64 oracle
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2516.6   # TFLOP/s, dense MFMA, MI355X published
+PEAK_FP8 = 5033.2    # TFLOP/s, dense MFMA, MI355X published
+WORKLOAD = dict(B=4, H=16, N=2048, d=128, causal=False)
+KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_14_amd", "csrc", "fa_fwd_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_B4H16N2048d128.json")
+
+
+def flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def time_calls(fn, steps, warmup):
+    """Average duration (ms) of fn() over `steps` calls, HIP events on the
+    current stream (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def device_qkv(B, H, N, d, seed, dist="normal"):
+    import fa_inputs
+    g = fa_inputs.make_qkv(B, H, N, d, seed, dist)
+    return tuple(fa_inputs.to_torch_bf16(x, "cuda") for x in (g.q_bits, g.k_bits, g.v_bits))
+
+
+def extras(fa):
+    import torch
+    import fa_inputs
+    out = []
+
+    def run(name, B, H, N, d, causal, seed, dtype=fa.FA_BF16, steps=20):
+        q, k, v = device_qkv(B, H, N, d, seed)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        ms = time_calls(lambda: fa.fwd(q, k, v, causal=causal, dtype=dtype, out=o, lse=lse),
+                        steps, 3)
+        tf = flops(B, H, N, d, causal) / (ms * 1e-3) / 1e12
+        peak = PEAK_BF16 if dtype == fa.FA_BF16 else PEAK_FP8
+        out.append({"name": name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                    "dtype": "bf16" if dtype == fa.FA_BF16 else "fp8_e4m3",
+                    "ms": round(ms, 4), "tflops": round(tf, 1),
+                    "pct_peak": round(100 * tf / peak, 1)})
+        del q, k, v, o, lse
+
+    run("mid causal", 4, 16, 2048, 128, True, fa_inputs.SEEDS["mid"])
+    for N in (512, 1024, 2048, 4096, 8192, 16384):
+        seed = fa_inputs.SEEDS["seq_sweep_base"] + int(math.log2(N // 512))
+        for causal in (False, True):
+            run("seq sweep", 16384 // N, 16, N, 128, causal, seed)
+    for i, d in enumerate((64, 96, 128, 256)):
+        run("head-dim sweep", 2, 16, 8192, d, True, fa_inputs.SEEDS["dim_sweep_base"] + i)
+    return out
+
+
+def cpu_baseline(budget_s=12.0):
+    """Times the float64 oracle on whole heads of the bench workload until
+    about `budget_s` seconds of CPU work have run."""
+    import numpy as np
+    import fa_inputs
+    from oracle import attention
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    B, H, N, d = WORKLOAD["B"], WORKLOAD["H"], WORKLOAD["N"], WORKLOAD["d"]
+    g = fa_inputs.make_qkv(B, H, N, d, fa_inputs.SEEDS["mid"])
+    q, k, v = g.q, g.k, g.v
+    heads = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and heads < B * H:
+        b, h = divmod(heads, H)
+        attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                  WORKLOAD["causal"])
+        heads += 1
+    dt = time.perf_counter() - t0
+    tf = heads * flops(1, 1, N, d, WORKLOAD["causal"]) / dt / 1e12
+    return {"value": round(tf, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {B * H} (batch, head) slices of B=4 H=16 N=2048 d=128 "
+                      f"non-causal, float64 NumPy, {dt:.1f} s"}
+
+
+def traffic_record():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    if rec.get("source_sha") != source_sha(KERNEL_SOURCE):
+        return None
+    return rec.get("traffic_bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy (reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every (batch, head) "
+              "is independent, so several GPUs would each run this kernel on their share.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_14_amd as fa
+    import fa_inputs
+
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    B, H, N, d, causal = (WORKLOAD[x] for x in ("B", "H", "N", "d", "causal"))
+    q, k, v = device_qkv(B, H, N, d, fa_inputs.SEEDS["mid"])
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    step = lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    f = flops(B, H, N, d, causal)
+    value = f / (ms_per_step * 1e-3) / 1e12
+    achieved = f / (kernel_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "attention fwd TFLOP/s (4BHN^2d, causal halved) + % of MFMA peak, bf16 & fp8",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attention fwd B=4 H=16 N=2048 d=128 bf16 non-causal",
+                   "global_batch": B, "seq_len": N, "heads": H, "head_dim": d,
+                   "causal": causal, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
+                     "traffic": traffic_record(), "kernel": "fwd_bf16_kernel<128,false>",
+                     "kernel_ms": round(kernel_ms, 5)},
+    }
+    del q, k, v, o, lse
+    if not args.no_extras:
+        rec["extra"] = extras(fa)
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

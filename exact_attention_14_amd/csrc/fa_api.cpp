@@ -27,7 +27,7 @@ bool fp8_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool pow2(int d) { return d > 0 && (d & (d - 1)) == 0; }
 
 int sizes_check(int B, int H, int N, int d) {
-  if ((long long)N * d >= (1LL << 31)) return FA_ERR_TOO_LARGE;
+  if ((long long)N * d > (1LL << 30)) return FA_ERR_TOO_LARGE;
   if ((long long)B * H >= (1LL << 31)) return FA_ERR_TOO_LARGE;
   return FA_OK;
 }

@@ -8,49 +8,115 @@
 // accumulator is rescaled by exp(m_prev - m_new), and P V is accumulated.
 // The normalisation by l happens once at the end. Causal query tiles stop at
 // the last key tile that holds a key at or before their last query (dibro.site
-// post, "Contribuciones clave").
+// post, "Contribuciones clave"). While one K/V tile is used the next one is
+// already being copied into the other half of a double buffer (dibro.site
+// post, "Arquitectura y metodo": two on-chip buffers in alternation; vikram-blog
+// post, "System Topology & Data Flow").
 //
 // gfx950 mapping
-//   * A workgroup owns Br = 128 queries of one (batch, head) as 4 waves of 32.
-//   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//     each lane then owns ONE query (lane % 32) and 16 of the 32 keys of a
-//     32-key block, so the row maximum and row sum are in-lane reductions
-//     plus one exchange with the other half of the wave.
+//   * A workgroup owns Br = 32*NW queries of one (batch, head): NW waves of 32.
+//   * K/V tiles of Bc = 64 keys move HBM -> LDS with buffer_load_dwordx4 ... lds
+//     (direct to LDS, no registers, zero-filled past the sequence end by the
+//     buffer's range check) into a two-stage LDS ring. Rows are 16-byte-chunk
+//     XOR-swizzled so that both read patterns below are free of bank conflicts.
+//   * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
+//     each lane owns ONE query (lane % 32) and 16 of the 32 keys of a 32-key
+//     block, so the row max and row sum are in-lane reductions plus one
+//     exchange with the other half of the wave. Q stays in registers.
 //   * The output is accumulated transposed too, O^T += V^T P^T, so the
-//     rescale by exp(m_prev - m_new) is a per-lane scalar.
-//   * P^T is fed to the second product straight from the registers that hold
-//     S^T. The reduction order over keys is free, so V is stored transposed in
-//     LDS with its key columns permuted (bits 2 and 3 of the key index swapped)
-//     to match the order in which P's registers hold the keys; each operand of
-//     the second product is then one 16-byte LDS read.
-//   * exp is evaluated as exp2 with scale*log2(e) folded into one FMA.
+//     rescale is a per-lane scalar, and P^T is fed from the very registers that
+//     held S^T. V stays row-major in LDS and is read transposed with
+//     ds_read_b64_tr_b16, whose lane order matches P's register order.
+//   * exp is evaluated as exp2 with scale*log2(e) folded into one FMA. The
+//     accumulator is rescaled only when some row maximum of the wave grew by
+//     more than 2^8 since the reference used so far; O and l always share the
+//     same reference, so the result is unchanged (exp values stay <= 2^8).
+//   * Workgroups are renumbered so that the query tiles of one (batch, head)
+//     run on one XCD (workgroups are dealt to the 8 XCDs round-robin), which
+//     keeps that head's K/V in one L2. Causal query tiles run longest first.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
 namespace {
 
-constexpr int kBR = 128;       // queries per workgroup
-constexpr int kBC = 64;        // keys per K/V tile
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kPad = 8;        // 16 bytes of padding per LDS row
+constexpr int kBC = 64;          // keys per K/V tile
+constexpr float kLazyLog2 = 8.f; // rescale threshold, log2 units
+// s_waitcnt immediate: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Column of key `key` (0..63 within a tile) in the transposed V tile.
-__device__ __forceinline__ int vt_col(int key) {
-  return (key & ~0xC) | ((key & 4) << 1) | ((key & 8) >> 1);
+template <int D>
+struct Geo {
+  static constexpr int CPR = D / 8;                                  // 16-B chunks of data per row
+  static constexpr int CPRP = D == 64 ? 8 : (D == 256 ? 32 : 16);    // chunk slots per LDS row
+  static constexpr int ROWB = CPRP * 16;                             // bytes per LDS row
+  static constexpr int TILEB = kBC * ROWB;                           // one K or V tile
+  static constexpr int STAGEB = 2 * TILEB;                           // K + V
+  static constexpr int NK = D / 16;                                  // k-steps of S^T = K Q^T
+  static constexpr int NO = D / 32;                                  // 32-row blocks of O^T
+};
+
+// Chunk-slot XOR for LDS row `row`; see the design notes for the bank model.
+template <int CPRP>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (CPRP == 8) {
+    const int s = row >> 1;
+    return ((s & 1) << 2) | ((s >> 1) & 3);
+  } else {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
-    const u16* __restrict__ Q, const u16* __restrict__ K,
-    const u16* __restrict__ V, u16* __restrict__ O, float* __restrict__ LSE,
-    int H, int N, int ntq, float scale) {
-  constexpr int KS = D + kPad;    // K tile row stride (elements)
-  constexpr int VS = kBC + kPad;  // transposed V tile row stride (elements)
-  constexpr int NK = D / 16;      // reduction steps of S^T = K Q^T
-  constexpr int NO = D / 32;      // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) u16 Ks[kBC * KS];
-  __shared__ __attribute__((aligned(16))) u16 Vt[D * VS];
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           kBufferFlags);
+}
+
+// Issue this wave's share of the direct-to-LDS copies of one K or V tile.
+template <int D, int NW>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile, int j0,
+                                          int wave, int lane) {
+  using G = Geo<D>;
+  constexpr int NI = G::CPRP / NW;  // 1 KiB wave copies per tile per wave
+  static_assert(NI >= 1 && G::CPRP % NW == 0, "tile split");
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int slot = (i * NW + wave) * 64 + lane;  // chunk slot in the tile
+    const int row = slot / G::CPRP;
+    const int c = (slot % G::CPRP) ^ swz<G::CPRP>(row);
+    const unsigned off = c < G::CPR ? ((unsigned)(j0 + row) * D + c * 8) * 2u : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(tile + (i * NW + wave) * 1024), 16, off,
+        0, 0, 0);
+  }
+}
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void fwd_bf16_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg, float scale) {
+  using G = Geo<D>;
+  constexpr int BR = 32 * NW;
+  // One LDS object per (stage, tensor): with the loop unrolled by two every
+  // read and every in-flight copy names a distinct object, so the compiler
+  // need not wait for the next tile's copies before reading the current one.
+  __shared__ __attribute__((aligned(1024))) char ks0[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vs0[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char ks1[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vs1[G::TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -58,65 +124,65 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // Workgroup -> (batch, head, query tile); causal tiles longest first.
+  // Workgroup id -> logical id with the tiles of one head on one XCD.
   const int bid = blockIdx.x;
-  const int qtr = bid % ntq;
-  const int bh = bid / ntq;
+  const int q8 = nwg >> 3, r8 = nwg & 7;
+  const int xcd = bid & 7, loc = bid >> 3;
+  const int lid = xcd < r8 ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
+  const int qtr = lid % ntq;
+  const int bh = lid / ntq;
   const int qt = CAUSAL ? (ntq - 1 - qtr) : qtr;
   const size_t head = (size_t)bh * (size_t)N;
-  const u16* Qh = Q + head * D;
-  const u16* Kh = K + head * D;
-  const u16* Vh = V + head * D;
+  const unsigned head_bytes = (unsigned)N * D * 2u;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head * D, head_bytes);
 
-  const int q0w = qt * kBR + wave * 32;  // first query of this wave
-  const int qi = q0w + l32;              // this lane's query
-  const bool qvalid = qi < N;
+  const int q0w = qt * BR + wave * 32;  // first query of this wave
+  const int qi = q0w + l32;             // this lane's query
+  const int q_last = min(N, qt * BR + BR) - 1;
+  const int ntiles = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
 
-  bf16x8 qreg[NK];
+  load_tile<D, NW>(rk, ks0, 0, wave, lane);
+  load_tile<D, NW>(rv, vs0, 0, wave, lane);
+
+  bf16x8 qreg[G::NK];
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    uint4 w = {0u, 0u, 0u, 0u};
-    if (qvalid) w = *(const uint4*)(Qh + (size_t)qi * D + kk * 16 + half * 8);
+  for (int kk = 0; kk < G::NK; ++kk) {
+    const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+        rq, (unsigned)(qi * D + kk * 16 + half * 8) * 2u, 0, 0);
     qreg[kk] = __builtin_bit_cast(bf16x8, w);
   }
 
-  f32x16 oacc[NO];
+  f32x16 oacc[G::NO];
 #pragma unroll
-  for (int i = 0; i < NO; ++i)
+  for (int i = 0; i < G::NO; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
-  float m_run = -INFINITY;  // running max of the raw scores q.k
-  float l_run = 0.f;        // this lane's half of the running row sum
+  float m_ref = -INFINITY;  // reference maximum (raw scores q.k) of O and l
+  float l_run = 0.f;        // this lane's half of the row sum
   const float c = scale * kLog2e;
 
-  const int q_last = min(N, qt * kBR + kBR) - 1;
-  const int ntiles = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
+  // Per-lane LDS byte offsets inside a tile.
+  const int krow = l32;                                   // + kb*32
+  const int kswz = swz<G::CPRP>(krow);
+  const int g16 = lane >> 4, i16 = lane & 15;             // tr16 lane group
+  const int vrow = 4 * half + (i16 >> 2);                 // + kb*32 + a*16 + r*8
+  const int vcol = (g16 & 1) * 2 + ((i16 & 3) >> 1);      // + blk*4 (chunk)
+  const int vbyte = (i16 & 1) * 8;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * kBC;
-    __syncthreads();  // previous tile fully consumed
-#pragma unroll
-    for (int it = 0; it < D / 32; ++it) {
-      const int id = it * kThreads + tid;
-      const int row = id / (D / 8), ch = id % (D / 8);
-      uint4 w = {0u, 0u, 0u, 0u};
-      if (j0 + row < N) w = *(const uint4*)(Kh + (size_t)(j0 + row) * D + ch * 8);
-      *(uint4*)(Ks + row * KS + ch * 8) = w;
-    }
-#pragma unroll
-    for (int it = 0; it < D / 32; ++it) {
-      const int id = it * kThreads + tid;
-      const int key = id % kBC, ch = id / kBC;
-      uint4 w = {0u, 0u, 0u, 0u};
-      if (j0 + key < N) w = *(const uint4*)(Vh + (size_t)(j0 + key) * D + ch * 8);
-      const u16* e = (const u16*)&w;
-      const int col = vt_col(key);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) Vt[(ch * 8 + x) * VS + col] = e[x];
-    }
+  // One K/V tile: kt/vt hold tile t, kn/vn receive tile t+1.
+  auto step = [&](const char* kt, const char* vt, char* kn, char* vn, int t) {
+    // This wave's copies of tile t have landed (vmcnt counts LDS-DMA copies);
+    // after the barrier every wave's have, and the other stage is free.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-
-    if (CAUSAL && j0 > q0w + 31) continue;  // every key after every query of this wave
+    if (t + 1 < ntiles) {
+      load_tile<D, NW>(rk, kn, (t + 1) * kBC, wave, lane);
+      load_tile<D, NW>(rv, vn, (t + 1) * kBC, wave, lane);
+    }
+    const int j0 = t * kBC;
+    if (CAUSAL && j0 > q0w + 31) return;  // every key after every query of this wave
 
     f32x16 s[2];
 #pragma unroll
@@ -125,8 +191,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(Ks + (kb * 32 + l32) * KS + kk * 16 + half * 8);
+      for (int kk = 0; kk < G::NK; ++kk) {
+        const int chunk = (2 * kk + half) ^ kswz;
+        const bf16x8 a =
+            *(const bf16x8*)(kt + (kb * 32 + krow) * G::ROWB + chunk * 16);
         acc = mfma32(a, qreg[kk], acc);
       }
       s[kb] = acc;
@@ -143,16 +211,25 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
         }
     }
 
-    float mx = s[0][0];
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+      for (int v = (kb == 0 ? 2 : 0); v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
     mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // no (-inf) - (-inf)
-    const float alpha = fast_exp2((m_run - m_use) * c);
-    const float mc = m_use * c;
+    // Move the reference when a row maximum exceeds it by more than 2^8 (or
+    // on the first keys a row sees); all lanes of the wave move together.
+    if (__any((mx - m_ref) * c > kLazyLog2)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < G::NO; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
+      m_ref = m_new;
+    }
+    const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
     float lsum = 0.f;
     bf16x8 p[2][2];
 #pragma unroll
@@ -163,31 +240,33 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
         lsum += e;
         p[kb][v / 8][v % 8] = (__bf16)e;
       }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < NO; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
+    l_run += lsum;
 
 #pragma unroll
-    for (int i = 0; i < NO; ++i)
+    for (int i = 0; i < G::NO; ++i)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
-          const bf16x8 vv =
-              *(const bf16x8*)(Vt + (i * 32 + l32) * VS + kb * 32 + a * 16 + half * 8);
-          oacc[i] = mfma32(vv, p[kb][a], oacc[i]);
+          const int row0 = kb * 32 + a * 16 + vrow;           // read r = 0
+          const int row1 = row0 + 8;                          // read r = 1
+          const int ch = i * 4 + vcol;
+          const char* lo = vt + row0 * G::ROWB + ((ch ^ swz<G::CPRP>(row0)) * 16) + vbyte;
+          const char* hi = vt + row1 * G::ROWB + ((ch ^ swz<G::CPRP>(row1)) * 16) + vbyte;
+          oacc[i] = mfma32(tr_pair(lo, hi), p[kb][a], oacc[i]);
         }
+    };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(ks0, vs0, ks1, vs1, t);
+    if (t + 1 < ntiles) step(ks1, vs1, ks0, vs0, t + 1);
   }
 
   const float l_tot = l_run + xor32(l_run);
   const float inv = 1.f / l_tot;
-  if (qvalid) {
+  if (qi < N) {
     u16* orow = O + (head + qi) * D;
 #pragma unroll
-    for (int i = 0; i < NO; ++i)
+    for (int i = 0; i < G::NO; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         bf16x4 w;
@@ -195,18 +274,21 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
         for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[i][4 * g + x] * inv);
         *(bf16x4*)(orow + i * 32 + 8 * g + 4 * half) = w;
       }
-    if (LSE != nullptr && half == 0) LSE[head + qi] = m_run * scale + __logf(l_tot);
+    if (LSE != nullptr && half == 0) LSE[head + qi] = m_ref * scale + __logf(l_tot);
   }
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse,
-                  int B, int H, int N, float scale, hipStream_t stream) {
-  const int ntq = (N + kBR - 1) / kBR;
+hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int H, int N, float scale, hipStream_t stream) {
+  constexpr int NW = 4;
+  constexpr int BR = 32 * NW;
+  const int ntq = (N + BR - 1) / BR;
   const long long nwg = (long long)ntq * B * H;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kThreads), 0,
-                     stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, H, N,
-                     ntq, scale);
+  if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+                     stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N, ntq,
+                     (int)nwg, scale);
   return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@ typedef enum fa_status {
     FA_ERR_UNSUPPORTED = -2,   /* head dimension or dtype not instantiated       */
     FA_ERR_MISALIGNED = -3,    /* a tensor pointer is not 16-byte aligned        */
     FA_ERR_HIP = -4,           /* the HIP runtime reported an error at launch    */
-    FA_ERR_TOO_LARGE = -5      /* N*d or B*H beyond the 32-bit index limits      */
+    FA_ERR_TOO_LARGE = -5      /* N*d above 2^30 or B*H above the 32-bit range  */
 } fa_status;
 
 /* Rows per FP8 quantisation block: one fp32 scale per 128 consecutive
@@ -71,7 +71,7 @@ typedef enum fa_status {
  *           fa_fwd_fp8 runs. d must be a power of two.
  * Validation order: null q/k/v/o -> INVALID_ARG; B, H or N < 1 -> INVALID_ARG;
  * dtype unknown or d unsupported -> UNSUPPORTED; scale not finite and > 0 ->
- * INVALID_ARG; N*d >= 2^31 or B*H >= 2^31 -> TOO_LARGE; a pointer not 16-byte
+ * INVALID_ARG; N*d > 2^30 or B*H >= 2^31 -> TOO_LARGE; a pointer not 16-byte
  * aligned -> MISALIGNED; launch (or scratch allocation) error -> HIP.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
