@@ -35,4 +35,31 @@ __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32);
 }
 
+// s_waitcnt immediate: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Raw buffer resource (gfx9 family dword 3: 32-bit data format). Loads at
+// byte offsets >= `bytes` return zeros without touching memory.
+constexpr int kBufferFlags = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           kBufferFlags);
+}
+
+// 16-byte copy HBM -> LDS for each lane; the wave writes 1 KiB contiguous at
+// `lds` (wave-uniform) + 16 * lane.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, void* lds,
+                                              unsigned byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds,
+                                           16, byte_off, 0, 0, 0);
+}
+
+// Workgroup id -> logical id such that consecutive logical ids run on one XCD
+// (the hardware deals workgroup ids to the 8 XCDs round-robin).
+__device__ __forceinline__ int xcd_grouped_id(int bid, int nwg) {
+  const int q8 = nwg >> 3, r8 = nwg & 7;
+  const int xcd = bid & 7, loc = bid >> 3;
+  return xcd < r8 ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
+}
+
 }  // namespace fa

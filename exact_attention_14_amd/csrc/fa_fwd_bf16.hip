@@ -42,8 +42,6 @@ namespace {
 
 constexpr int kBC = 64;          // keys per K/V tile
 constexpr float kLazyLog2 = 8.f; // rescale threshold, log2 units
-// s_waitcnt immediate: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
-constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <int D>
 struct Geo {
@@ -78,13 +76,6 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
   return __builtin_bit_cast(bf16x8, c);
 }
 
-constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                           kBufferFlags);
-}
-
 // Issue this wave's share of the direct-to-LDS copies of one K or V tile.
 template <int D, int NW>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile, int j0,
@@ -98,9 +89,7 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile,
     const int row = slot / G::CPRP;
     const int c = (slot % G::CPRP) ^ swz<G::CPRP>(row);
     const unsigned off = c < G::CPR ? ((unsigned)(j0 + row) * D + c * 8) * 2u : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(tile + (i * NW + wave) * 1024), 16, off,
-        0, 0, 0);
+    copy16_to_lds(rs, tile + (i * NW + wave) * 1024, off);
   }
 }
 
@@ -125,10 +114,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
   const int l32 = lane & 31;
 
   // Workgroup id -> logical id with the tiles of one head on one XCD.
-  const int bid = blockIdx.x;
-  const int q8 = nwg >> 3, r8 = nwg & 7;
-  const int xcd = bid & 7, loc = bid >> 3;
-  const int lid = xcd < r8 ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
+  const int lid = xcd_grouped_id(blockIdx.x, nwg);
   const int qtr = lid % ntq;
   const int bh = lid / ntq;
   const int qt = CAUSAL ? (ntq - 1 - qtr) : qtr;
