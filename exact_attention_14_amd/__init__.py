@@ -36,6 +36,11 @@ class FAError(RuntimeError):
 
 
 def _load():
+    # torch brings its own HIP runtime (soname libamdhip64.so.7, requested as
+    # libamdhip64.so). Importing it first makes libfa.so bind to that same
+    # runtime; loaded the other way round the process would hold two HIP
+    # runtimes and the library's launches would not see torch's device memory.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it first with "

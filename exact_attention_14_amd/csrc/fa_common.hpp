@@ -54,6 +54,32 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, void* l
                                            16, byte_off, 0, 0, 0);
 }
 
+// Buffer resource as four dwords for inline assembly (base, stride 0,
+// num_records = bytes, gfx9 dword 3).
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* p, unsigned bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(p);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xFFFF);
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = kBufferFlags;
+  return r;
+}
+
+// The same 16-byte HBM -> LDS copy, written as assembly so that the compiler
+// does not treat it as an LDS store: it then inserts no conservative
+// vmcnt(0) before unrelated LDS reads, and the kernel's own s_waitcnt
+// vmcnt(n) decides when a copy is complete. `lds` must be wave-uniform. The
+// instruction has no register results (the data goes to LDS).
+__device__ __forceinline__ void copy16_to_lds_asm(i32x4 rsrc, const void* lds, unsigned byte_off) {
+  const unsigned m0 = (unsigned)reinterpret_cast<unsigned long long>(
+      (const __attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(byte_off), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Workgroup id -> logical id such that consecutive logical ids run on one XCD
 // (the hardware deals workgroup ids to the 8 XCDs round-robin).
 __device__ __forceinline__ int xcd_grouped_id(int bid, int nwg) {

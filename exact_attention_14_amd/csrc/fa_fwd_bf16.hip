@@ -34,6 +34,9 @@
 //   * Workgroups are renumbered so that the query tiles of one (batch, head)
 //     run on one XCD (workgroups are dealt to the 8 XCDs round-robin), which
 //     keeps that head's K/V in one L2. Causal query tiles run longest first.
+#include <cstdlib>
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -42,6 +45,10 @@ namespace {
 
 constexpr int kBC = 64;          // keys per K/V tile
 constexpr float kLazyLog2 = 8.f; // rescale threshold, log2 units
+// Instruction classes of __builtin_amdgcn_sched_group_barrier masks.
+constexpr int kSchedValu = 0x002 | 0x400;  // VALU and transcendental
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 template <int D>
 struct Geo {
@@ -93,8 +100,43 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile,
   }
 }
 
+// Byte offsets past any head buffer (head buffers are at most 2 GiB): loads
+// there return zeros without memory traffic. Chunk slots beyond the data
+// width (d = 96) use kPadOffset; whole tiles past the end use kOutOfRange.
+constexpr unsigned kPadOffset = 0x40000000u;
+constexpr unsigned kOutOfRange = 0x80000000u;
+
+// s_waitcnt immediate for vmcnt = n (n < 64), expcnt and lgkmcnt at maxima.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Per-lane byte offsets (tile row 0) of this wave's share of a tile copy;
+// rows past the data width get an offset beyond any buffer (zero fill).
+template <int D, int NW>
+struct TileCopy {
+  static constexpr int NI = Geo<D>::CPRP / NW;
+  unsigned off[NI];
+  __device__ __forceinline__ TileCopy(int wave, int lane) {
+    using G = Geo<D>;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int slot = (i * NW + wave) * 64 + lane;
+      const int row = slot / G::CPRP;
+      const int c = (slot % G::CPRP) ^ swz<G::CPRP>(row);
+      off[i] = c < G::CPR ? (unsigned)(row * D + c * 8) * 2u : kPadOffset;
+    }
+  }
+  // Copy the tile starting at key row j0 into `tile` (zeros if !valid).
+  __device__ __forceinline__ void issue(i32x4 rs, char* tile, int j0, int wave,
+                                        bool valid = true) const {
+    const unsigned base = valid ? (unsigned)j0 * D * 2u : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      copy16_to_lds_asm(rs, tile + (i * NW + wave) * 1024, off[i] + base);
+  }
+};
+
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void fwd_bf16_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void fwd_bf16_v2_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg, float scale) {
   using G = Geo<D>;
@@ -264,15 +306,262 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
   }
 }
 
+// Exchange-and-max with the lane 32 positions away (v_permlane32_swap).
+__device__ __forceinline__ float max_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Software-pipelined kernel: while the softmax of tile t runs on the VALU,
+// the scores of tile t+1 are already being formed on the matrix cores, and
+// the P V products of tile t overlap the second half of its softmax (QbitAI
+// article: two-stage GEMM-softmax pipelining, S_cur / S_next). K is copied
+// one tile further ahead than V through two-stage LDS rings; the copies are
+// issued as assembly so that only the kernel's own waits order them.
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg, float scale) {
+  using G = Geo<D>;
+  using CP = TileCopy<D, NW>;
+  constexpr int BR = 32 * NW;
+  // K_j lives in ks[j % 2], V_j in vs[j % 2]. The copies are issued as
+  // assembly, so the compiler adds no waits of its own for them.
+  __shared__ __attribute__((aligned(1024))) char ks0[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vs0[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char ks1[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vs1[G::TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int lid = xcd_grouped_id(blockIdx.x, nwg);
+  const int qtr = lid % ntq;
+  const int bh = lid / ntq;
+  const int qt = CAUSAL ? (ntq - 1 - qtr) : qtr;
+  const size_t head = (size_t)bh * (size_t)N;
+  const unsigned head_bytes = (unsigned)N * D * 2u;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head * D, head_bytes);
+  const i32x4 rk = make_rsrc_words(K + head * D, head_bytes);
+  const i32x4 rv = make_rsrc_words(V + head * D, head_bytes);
+
+  const int q0w = qt * BR + wave * 32;
+  const int qi = q0w + l32;
+  const int q_last = min(N, qt * BR + BR) - 1;
+  const int T = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
+
+  // Prologue, in this order: copy K_0, load Q, copy V_0 and K_1. (The
+  // compiler's waits for Q then cover K_0 but not the later copies.)
+  const CP cp(wave, lane);
+  cp.issue(rk, ks0, 0, wave, true);
+  bf16x8 qreg[G::NK];
+#pragma unroll
+  for (int kk = 0; kk < G::NK; ++kk) {
+    const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+        rq, (unsigned)(qi * D + kk * 16 + half * 8) * 2u, 0, 0);
+    qreg[kk] = __builtin_bit_cast(bf16x8, w);
+  }
+  cp.issue(rv, vs0, 0, wave, true);
+  cp.issue(rk, ks1, kBC, wave, T > 1);
+
+  f32x16 oacc[G::NO];
+#pragma unroll
+  for (int i = 0; i < G::NO; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
+  float m_ref = -INFINITY;  // reference maximum (raw scores) of O and l
+  float l_run = 0.f;
+  const float c = scale * kLog2e;
+
+  // Loop-invariant per-lane LDS byte offsets. The swizzle of a row depends
+  // only on its low 4 bits, which the 32- and 16-row block offsets keep, so
+  // those offsets (and the stage base) fold into instruction immediates.
+  int koff[G::NK];
+  {
+    const int kswz = swz<G::CPRP>(l32);
+#pragma unroll
+    for (int kk = 0; kk < G::NK; ++kk) koff[kk] = l32 * G::ROWB + (((2 * kk + half) ^ kswz) << 4);
+  }
+  int voff[G::NO][2];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int vrow = 4 * half + (i16 >> 2);
+    const int vcol = (g16 & 1) * 2 + ((i16 & 3) >> 1);
+    const int vbyte = (i16 & 1) * 8;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = vrow + 8 * r;
+      const int sw = swz<G::CPRP>(row);
+#pragma unroll
+      for (int i = 0; i < G::NO; ++i)
+        voff[i][r] = row * G::ROWB + (((i * 4 + vcol) ^ sw) << 4) + vbyte;
+    }
+  }
+
+  auto scores = [&](const char* kt, f32x16* s) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < G::NK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(kt + kb * 32 * G::ROWB + koff[kk]);
+        s[kb] = mfma32(a, qreg[kk], s[kb]);
+      }
+  };
+  auto mask = [&](f32x16* s, int j0) {
+    if ((j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > q0w)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = j0 + kb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+          if (key >= N || (CAUSAL && key > qi)) s[kb][v] = -INFINITY;
+        }
+    }
+  };
+  auto rowmax = [&](const f32x16* s) {
+    float a = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = (kb == 0 ? 2 : 0); v < 16; ++v) a = fmaxf(a, s[kb][v]);
+    return max_with_other_half(a);
+  };
+  auto pv = [&](const char* vt, int kb, const bf16x8* p) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < G::NO; ++i) {
+        const char* blk = vt + (kb * 32 + a * 16) * G::ROWB;
+        oacc[i] = mfma32(tr_pair(blk + voff[i][0], blk + voff[i][1]), p[a], oacc[i]);
+      }
+  };
+
+  f32x16 s_cur[2], s_nxt[2];
+  // K_0 has landed once at most the Q loads and the two younger copies (all
+  // issued after it) are still in flight.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(G::NK + 2 * CP::NI));
+  __syncthreads();
+  scores(ks0, s_cur);
+  mask(s_cur, 0);
+  float mt = rowmax(s_cur);
+
+  // Tile t: S_t is in s_cur with its row max in mt; K_{t+1} (kr) and V_t (vr)
+  // are in LDS once every wave passed the barrier; K_{t+2} goes to kl, V_{t+1}
+  // to vl. The last tile forms scores of a tile T that are discarded.
+  auto step = [&](const char* kr, const char* vr, char* kl, char* vl, int t) {
+    // This wave's copies of K_{t+1} and V_t have landed; after the barrier
+    // every wave's have, and the stages of K_t and V_{t-1} are free.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    cp.issue(rk, kl, (t + 2) * kBC, wave, t + 2 < T);
+    cp.issue(rv, vl, (t + 1) * kBC, wave, t + 1 < T);
+    if (__any((mt - m_ref) * c > kLazyLog2)) {
+      const float m_new = fmaxf(m_ref, mt);
+      const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < G::NO; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
+      m_ref = m_new;
+    }
+    const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+    bf16x8 p[2][2];
+    float lsum = 0.f;
+    auto softmax_half = [&](int kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float e = fast_exp2(fmaf(s_cur[kb][v], c, -mc));
+        lsum += e;
+        p[kb][v / 8][v % 8] = (__bf16)e;
+      }
+    };
+    // Stage A: scores of tile t+1 on the matrix cores, first half of the
+    // softmax of tile t on the VALU.
+    scores(kr, s_nxt);
+    softmax_half(0);
+    // Issue order: K fragment reads run two MFMAs ahead; each MFMA is
+    // followed by four VALU/transcendental instructions of the softmax.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * G::NK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    // Stage B: P V of tile t and the second half of its softmax.
+    pv(vr, 0, p[0]);
+    softmax_half(1);
+    pv(vr, 1, p[1]);
+    l_run += lsum;
+    // Issue order: V fragment reads run two MFMAs ahead; each MFMA is
+    // followed by four VALU/transcendental instructions.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * G::NO; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    mask(s_nxt, (t + 1) * kBC);  // a wave-uniform branch, taken on edge tiles only
+    mt = rowmax(s_nxt);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+  };
+
+  for (int t = 0; t < T; t += 2) {
+    step(ks1, vs0, ks0, vs1, t);
+    if (t + 1 < T) step(ks0, vs1, ks1, vs0, t + 1);
+  }
+  // No copy may land in LDS after the workgroup exits.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = 1.f / l_tot;
+  if (qi < N) {
+    u16* orow = O + (head + qi) * D;
+#pragma unroll
+    for (int i = 0; i < G::NO; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[i][4 * g + x] * inv);
+        *(bf16x4*)(orow + i * 32 + 8 * g + 4 * half) = w;
+      }
+    if (LSE != nullptr && half == 0) LSE[head + qi] = m_ref * scale + __logf(l_tot);
+  }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int N, float scale, hipStream_t stream) {
-  constexpr int NW = 4;
-  constexpr int BR = 32 * NW;
-  const int ntq = (N + BR - 1) / BR;
+  static const bool use_v2 = [] {
+    const char* e = std::getenv("FA_BF16_KERNEL");
+    return e != nullptr && e[0] == 'v' && e[1] == '2';
+  }();
+  const bool v2 = use_v2 || D == 256;
+  const int NW = 4;
+  const int ntq = (N + 32 * NW - 1) / (32 * NW);
   const long long nwg = (long long)ntq * B * H;
   if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+  if constexpr (D != 256) {
+    if (!v2) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)nwg), dim3(4 * 64), 0,
+                         stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N,
+                         ntq, (int)nwg, scale);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_bf16_v2_kernel<D, CAUSAL, 4>), dim3((unsigned)nwg), dim3(4 * 64), 0,
                      stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N, ntq,
                      (int)nwg, scale);
   return hipGetLastError();
