@@ -12,6 +12,8 @@
 // is presented transposed to the second product because the FP8 matrix
 // instruction wants the reduction dimension contiguous (QbitAI article, FP8
 // section).
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -205,6 +207,17 @@ __device__ __forceinline__ int swz8(int row) {
   }
 }
 
+// Byte offset past any head buffer: copies there return zeros, no traffic.
+constexpr unsigned kOutOfRange8 = 0x80000000u;
+
+// s_waitcnt immediate for vmcnt = n (n < 64), expcnt and lgkmcnt at maxima.
+constexpr int waitcnt_vm8(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier masks.
+constexpr int kSchedValu = 0x002 | 0x400;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 template <int D, int NW>
 __device__ __forceinline__ void load_tile8(__amdgpu_buffer_rsrc_t rs, char* tile, int j0,
                                            int wave, int lane) {
@@ -235,6 +248,47 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// Per-lane byte offsets (tile row 0) of this wave's share of an e4m3 tile copy.
+template <int D, int NW>
+struct TileCopy8 {
+  using G = Geo8<D>;
+  static constexpr int NCH = kBC * G::CPR;                 // 16-byte chunks per tile
+  static constexpr int NI = (NCH + 64 * NW - 1) / (64 * NW);
+  unsigned off[NI];
+  __device__ __forceinline__ TileCopy8(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int slot = (i * NW + wave) * 64 + lane;
+      const int row = slot / G::CPR;
+      const int c = (slot % G::CPR) ^ swz8<D>(row);
+      off[i] = slot < NCH ? (unsigned)(row * D + c * 16) : kOutOfRange8;
+    }
+  }
+  static_assert(NCH % (64 * NW) == 0, "every wave issues the same number of copies");
+  __device__ __forceinline__ void issue(i32x4 rs, char* tile, int j0, int wave, bool valid) const {
+    const unsigned base = valid ? (unsigned)j0 * D : kOutOfRange8;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      copy16_to_lds_asm(rs, tile + (i * NW + wave) * 1024, off[i] + base);
+  }
+};
+
+// Exchange-and-max with the lane 32 positions away (v_permlane32_swap).
+__device__ __forceinline__ float max_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Same software pipeline as the bf16 kernel: while the VALU runs the
+// softmax of tile t, the matrix cores form the scores of tile t+1; the P V
+// products of tile t then overlap the row maxima of tile t+1.
+//   * P * 2^8 comes straight out of exp2 (8 is added to the exponent).
+//   * The row sum is taken by one more e4m3 product, ones(32 x 64) . P^T,
+//     whose every output row is sum_k P*2^8 for the lane's query: the sum of
+//     exactly the probabilities the P V product used.
+//   * The reference maximum moves only when a row maximum exceeds it by more
+//     than 0.75 (log2 units), so P * 2^8 <= 2^8.75 = 430 stays within e4m3.
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
 void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
@@ -243,7 +297,9 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
                     u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg,
                     int nblk, float scale) {
   using G = Geo8<D>;
+  using CP = TileCopy8<D, NW>;
   constexpr int BR = 32 * NW;
+  constexpr float kLazy = 0.75f;
   __shared__ __attribute__((aligned(1024))) char ks0[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char vs0[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char ks1[G::TILEB];
@@ -251,7 +307,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -262,8 +318,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   const size_t head = (size_t)bh * (size_t)N;
   const unsigned head_bytes = (unsigned)N * D;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q8 + head * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K8 + head * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V8 + head * D, head_bytes);
+  const i32x4 rk = make_rsrc_words(K8 + head * D, head_bytes);
+  const i32x4 rv = make_rsrc_words(V8 + head * D, head_bytes);
   const float* sqh = SQ + (size_t)bh * nblk;
   const float* skh = SK + (size_t)bh * nblk;
   const float* svh = SV + (size_t)bh * nblk;
@@ -271,11 +327,11 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   const int q0w = qt * BR + wave * 32;
   const int qi = q0w + l32;
   const int q_last = min(N, qt * BR + BR) - 1;
-  const int ntiles = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
+  const int T = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
 
-  load_tile8<D, NW>(rk, ks0, 0, wave, lane);
-  load_tile8<D, NW>(rv, vs0, 0, wave, lane);
-
+  // Prologue: copy K_0, load Q, copy V_0 and K_1.
+  const CP cp(wave, lane);
+  cp.issue(rk, ks0, 0, wave, true);
   i32x8 qreg[G::NKS];
 #pragma unroll
   for (int ks = 0; ks < G::NKS; ++ks) {
@@ -284,6 +340,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     const i32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
     qreg[ks] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+  cp.issue(rv, vs0, 0, wave, true);
+  cp.issue(rk, ks1, kBC, wave, T > 1);
   const float sq = sqh[min(qi, N - 1) / kBlock];
 
   f32x16 oacc[G::NO];
@@ -291,48 +349,54 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   for (int i = 0; i < G::NO; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
-  // Softmax state in log2 units of the scaled score: z = scale * log2(e) * q.k.
-  float m_ref = -INFINITY;
-  float l_run = 0.f;
-  float sv_cur = 1.f;  // V scale the accumulator is expressed in
+  f32x16 lacc;  // every element: sum of P * 2^8 (only element 0 is read)
+#pragma unroll
+  for (int v = 0; v < 16; ++v) lacc[v] = 0.f;
+  float m_ref = -INFINITY;  // reference maximum, log2 units of scale * q.k
+  float sv_cur = 1.f;       // V scale the accumulator is expressed in
   const float c = scale * kLog2e;
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
-  const int krow = l32;
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int vq = i16 & 1, vt = i16 >> 1;  // tr8 source lane = 2 * vt + vq
-  const int vrow = 8 * (vt >> 2) + 4 * half + (vt & 3);  // + 16 * r
-
-  auto step = [&](const char* kt, const char* vt_, char* kn, char* vn, int t) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      load_tile8<D, NW>(rk, kn, (t + 1) * kBC, wave, lane);
-      load_tile8<D, NW>(rv, vn, (t + 1) * kBC, wave, lane);
+  // Loop-invariant per-lane LDS offsets (row swizzles depend on row & 15 only).
+  int koff[G::NKS][2];
+  {
+    const int sw = swz8<D>(l32);
+#pragma unroll
+    for (int ks = 0; ks < G::NKS; ++ks)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) koff[ks][u] = l32 * G::ROWB + (((ks * 4 + 2 * half + u) ^ sw) << 4);
+  }
+  int voff[G::NO];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int vq = i16 & 1, vt = i16 >> 1;  // tr8 source lane = 2 * vt + vq
+    const int vrow = 8 * (vt >> 2) + 4 * half + (vt & 3);
+    const int sw = swz8<D>(vrow);
+#pragma unroll
+    for (int i = 0; i < G::NO; ++i) {
+      const int d = i * 32 + 16 * (g16 & 1) + 8 * vq;
+      voff[i] = vrow * G::ROWB + (((d >> 4) ^ sw) << 4) + (d & 15);
     }
-    const int j0 = t * kBC;
-    if (CAUSAL && j0 > q0w + 31) return;
+  }
 
-    f32x16 s[2];
+  auto scores = [&](const char* kt, f32x16* s) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-      const int row = kb * 32 + krow;
-      const int sw = swz8<D>(row);
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < G::NKS; ++ks) {
-        const int c0 = (ks * 4 + 2 * half) ^ sw;
-        const int c1 = (ks * 4 + 2 * half + 1) ^ sw;
-        const i32x4 lo = *(const i32x4*)(kt + row * G::ROWB + c0 * 16);
-        const i32x4 hi = *(const i32x4*)(kt + row * G::ROWB + c1 * 16);
-        acc = mfma8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qreg[ks], acc);
+    for (int ks = 0; ks < G::NKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const char* row = kt + kb * 32 * G::ROWB;
+        const i32x4 lo = *(const i32x4*)(row + koff[ks][0]);
+        const i32x4 hi = *(const i32x4*)(row + koff[ks][1]);
+        s[kb] = mfma8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qreg[ks], s[kb]);
       }
-      s[kb] = acc;
-    }
-
-    const bool need_mask = (j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > q0w);
-    if (need_mask) {
+  };
+  auto mask = [&](f32x16* s, int j0) {
+    if ((j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > q0w)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -341,22 +405,40 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
           if (key >= N || (CAUSAL && key > qi)) s[kb][v] = -INFINITY;
         }
     }
-
-    const float cs = c * sq * skh[j0 / kBlock];  // raw MFMA result -> log2 units
-    const float sv_t = svh[j0 / kBlock];
-    float mx = fmaxf(s[0][0], s[0][1]);
+  };
+  auto rowmax = [&](const f32x16* s) {
+    float a = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = (kb == 0 ? 2 : 0); v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = fmaxf(mx, xor32(mx)) * cs;
-    // Exact running maximum (P * 2^8 must stay within e4m3), and the
-    // accumulator re-expressed in the V scale of this tile.
-    if (__any(mx > m_ref) || sv_t != sv_cur) {
+      for (int v = (kb == 0 ? 2 : 0); v < 16; ++v) a = fmaxf(a, s[kb][v]);
+    return max_other_half(a);
+  };
+
+  f32x16 s_cur[2], s_nxt[2];
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm8(2 * G::NKS + 2 * CP::NI));  // K_0 landed
+  __syncthreads();
+  scores(ks0, s_cur);
+  mask(s_cur, 0);
+  float mt = rowmax(s_cur);  // raw row max of the tile about to be processed
+
+  // MASK: whether the scores of tile t+1 may need masking (edge tiles only;
+  // the steady-state loop runs without the branch).
+  auto step = [&](auto mask_tag, const char* kr, const char* vr, char* kl, char* vl, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // K_{t+1} and V_t landed
+    __syncthreads();
+    cp.issue(rk, kl, (t + 2) * kBC, wave, t + 2 < T);
+    cp.issue(rv, vl, (t + 1) * kBC, wave, t + 1 < T);
+    const int j0 = t * kBC;
+    const float cs = c * sq * skh[min(j0, N - 1) / kBlock];  // raw MFMA result -> log2 units
+    const float sv_t = svh[min(j0, N - 1) / kBlock];
+    const float mx = mt * cs;
+    if (__any(mx - m_ref > kLazy) || sv_t != sv_cur) {
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m_new);
       const float f = alpha * (sv_cur / sv_t);
-      l_run *= alpha;
+      lacc[0] *= alpha;
 #pragma unroll
       for (int i = 0; i < G::NO; ++i)
 #pragma unroll
@@ -364,47 +446,63 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
       m_ref = m_new;
       sv_cur = sv_t;
     }
-    const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
-    float lsum = 0.f;
-    int pw[8];  // P * 2^8 as e4m3, byte b = kb * 16 + v
+    const float mb = 8.f - ((m_ref == -INFINITY) ? 0.f : m_ref);  // exponent offset
+    // Stage A: scores of tile t+1; softmax of tile t -> P * 2^8 as e4m3.
+    scores(kr, s_nxt);
+    int pw[8];  // byte b = kb * 16 + v
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         float e[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          e[x] = fast_exp2(fmaf(s[kb][4 * v4 + x], cs, -mref));
-          lsum += e[x];
-        }
-        const int w = cvt_pk_fp8<false>(e[0] * kPScale, e[1] * kPScale, 0);
-        pw[kb * 4 + v4] = cvt_pk_fp8<true>(e[2] * kPScale, e[3] * kPScale, w);
+        for (int x = 0; x < 4; ++x) e[x] = fast_exp2(fmaf(s_cur[kb][4 * v4 + x], cs, mb));
+        const int w = cvt_pk_fp8<false>(e[0], e[1], 0);
+        pw[kb * 4 + v4] = cvt_pk_fp8<true>(e[2], e[3], w);
       }
-    l_run += lsum;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * G::NKS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 10, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    // Nothing moves across: keeps stage B's V fragments out of stage A.
+    __builtin_amdgcn_sched_barrier(0);
     const i32x8 pv = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-
+    // Stage B: P V of tile t and the row sums; then the next tile's row max.
 #pragma unroll
     for (int i = 0; i < G::NO; ++i) {
-      const int d = i * 32 + 16 * (g16 & 1) + 8 * vq;
-      i32x2 part[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * r + vrow;
-        const int ch = (d >> 4) ^ swz8<D>(row);
-        part[r] = tr8(vt_ + row * G::ROWB + ch * 16 + (d & 15));
-      }
-      const i32x8 a = {part[0][0], part[0][1], part[1][0], part[1][1],
-                       part[2][0], part[2][1], part[3][0], part[3][1]};
+      const char* base = vr + voff[i];
+      const i32x2 p0 = tr8(base);
+      const i32x2 p1 = tr8(base + 16 * G::ROWB);
+      const i32x2 p2 = tr8(base + 32 * G::ROWB);
+      const i32x2 p3 = tr8(base + 48 * G::ROWB);
+      const i32x8 a = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       oacc[i] = mfma8(a, pv, oacc[i]);
     }
+    lacc = mfma8(ones, pv, lacc);
+    if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
+    mt = rowmax(s_nxt);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(ks0, vs0, ks1, vs1, t);
-    if (t + 1 < ntiles) step(ks1, vs1, ks0, vs0, t + 1);
+  // Tiles j < J need no mask for any wave: every key of them precedes the
+  // workgroup's first query (causal) and lies inside the sequence.
+  const int J = CAUSAL ? min(N / kBC, (qt * BR + 1) / kBC) : N / kBC;
+  int t = 0;
+  for (; t + 2 < J; t += 2) {  // steps whose next tile (t+1, t+2) is unmasked
+    step(std::false_type{}, ks1, vs0, ks0, vs1, t);
+    step(std::false_type{}, ks0, vs1, ks1, vs0, t + 1);
   }
+  for (; t < T; t += 2) {  // t is even here: stage parity stays static
+    step(std::true_type{}, ks1, vs0, ks0, vs1, t);
+    if (t + 1 < T) step(std::true_type{}, ks0, vs1, ks1, vs0, t + 1);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // no copy lands after the exit
 
-  const float l_tot = l_run + xor32(l_run);
-  const float inv = sv_cur / (kPScale * l_tot);
+  const float l_tot = lacc[0];  // sum of P * 2^8
+  const float inv = sv_cur / l_tot;
   if (qi < N) {
     u16* orow = O + (head + qi) * D;
 #pragma unroll
@@ -416,7 +514,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
         for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[i][4 * g + x] * inv);
         *(bf16x4*)(orow + i * 32 + 8 * g + 4 * half) = w;
       }
-    if (LSE != nullptr && half == 0) LSE[head + qi] = (m_ref + __log2f(l_tot)) * kLn2;
+    if (LSE != nullptr && half == 0) LSE[head + qi] = (m_ref + __log2f(l_tot) - 8.f) * kLn2;
   }
 }
 

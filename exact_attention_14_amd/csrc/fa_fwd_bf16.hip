@@ -456,7 +456,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // Tile t: S_t is in s_cur with its row max in mt; K_{t+1} (kr) and V_t (vr)
   // are in LDS once every wave passed the barrier; K_{t+2} goes to kl, V_{t+1}
   // to vl. The last tile forms scores of a tile T that are discarded.
-  auto step = [&](const char* kr, const char* vr, char* kl, char* vl, int t) {
+  // MASK: whether the scores of tile t+1 may need masking (edge tiles only;
+  // the steady-state loop runs without the branch).
+  auto step = [&](auto mask_tag, const char* kr, const char* vr, char* kl, char* vl, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     // This wave's copies of K_{t+1} and V_t have landed; after the barrier
     // every wave's have, and the stages of K_t and V_{t-1} are free.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -497,6 +500,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
+    // Nothing moves across: keeps stage B's V fragments out of stage A.
+    __builtin_amdgcn_sched_barrier(0);
     // Stage B: P V of tile t and the second half of its softmax.
     pv(vr, 0, p[0]);
     softmax_half(1);
@@ -511,15 +516,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
-    mask(s_nxt, (t + 1) * kBC);  // a wave-uniform branch, taken on edge tiles only
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
     mt = rowmax(s_nxt);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
   };
 
-  for (int t = 0; t < T; t += 2) {
-    step(ks1, vs0, ks0, vs1, t);
-    if (t + 1 < T) step(ks0, vs1, ks1, vs0, t + 1);
+  // Tiles j < J need no mask for any wave: every key of them precedes the
+  // workgroup's first query (causal) and lies inside the sequence.
+  const int J = CAUSAL ? min(N / kBC, (qt * BR + 1) / kBC) : N / kBC;
+  int t = 0;
+  for (; t + 2 < J; t += 2) {  // steps whose next tile (t+1, t+2) is unmasked
+    step(std::false_type{}, ks1, vs0, ks0, vs1, t);
+    step(std::false_type{}, ks0, vs1, ks1, vs0, t + 1);
+  }
+  for (; t < T; t += 2) {  // t is even here: stage parity stays static
+    step(std::true_type{}, ks1, vs0, ks0, vs1, t);
+    if (t + 1 < T) step(std::true_type{}, ks0, vs1, ks1, vs0, t + 1);
   }
   // No copy may land in LDS after the workgroup exits.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

@@ -116,7 +116,9 @@ int fa_quant_fp8(const void* x, void* x8, float* scales,
  *              v_scale : float32 [B, H, ceil(N/128)] as fa_quant_fp8 writes.
  * o : bf16 [B, H, N, d]; lse : float32 [B, H, N] or NULL; d : 64, 128, 256.
  * The probabilities P are multiplied by 256 and rounded to e4m3 for the P V
- * product; the row sum uses the unrounded float32 P.
+ * product; the row sum is the float32 accumulation of those same rounded
+ * values (taken on the matrix cores), so O is normalised by the weights it
+ * was formed with.
  * Validation order as fa_fwd (null scale arrays -> INVALID_ARG).
  */
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
