@@ -320,7 +320,7 @@ __device__ __forceinline__ float max_with_other_half(float x) {
 // one tile further ahead than V through two-stage LDS rings; the copies are
 // issued as assembly so that only the kernel's own waits order them.
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg, float scale) {
   using G = Geo<D>;
@@ -562,18 +562,16 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     const char* e = std::getenv("FA_BF16_KERNEL");
     return e != nullptr && e[0] == 'v' && e[1] == '2';
   }();
-  const bool v2 = use_v2 || D == 256;
+  const bool v2 = use_v2;
   const int NW = 4;
   const int ntq = (N + 32 * NW - 1) / (32 * NW);
   const long long nwg = (long long)ntq * B * H;
   if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
-  if constexpr (D != 256) {
-    if (!v2) {
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)nwg), dim3(4 * 64), 0,
-                         stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N,
-                         ntq, (int)nwg, scale);
-      return hipGetLastError();
-    }
+  if (!v2) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)nwg), dim3(4 * 64), 0,
+                       stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N, ntq,
+                       (int)nwg, scale);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((fwd_bf16_v2_kernel<D, CAUSAL, 4>), dim3((unsigned)nwg), dim3(4 * 64), 0,
                      stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N, ntq,
