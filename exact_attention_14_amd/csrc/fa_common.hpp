@@ -80,6 +80,26 @@ __device__ __forceinline__ void copy16_to_lds_asm(i32x4 rsrc, const void* lds, u
                : "memory", "m0");
 }
 
+// Workgroup id -> (head, query-tile rank). Workgroup ids are dealt to the 8
+// XCDs round-robin. With hpx > 0 (B*H = 8*hpx heads) each XCD owns hpx whole
+// heads and starts its workgroups in rank order across them (rank 0 = the
+// longest causal tile first); otherwise consecutive logical ids, i.e. the
+// tiles of one head, run on one XCD.
+__device__ __forceinline__ void tile_of_workgroup(int bid, int nwg, int ntq, int hpx, int& bh,
+                                                  int& rank) {
+  if (hpx > 0) {
+    const int loc = bid >> 3;
+    rank = loc / hpx;
+    bh = (bid & 7) * hpx + loc % hpx;
+    return;
+  }
+  const int q8 = nwg >> 3, r8 = nwg & 7;
+  const int xcd = bid & 7, loc = bid >> 3;
+  const int lid = xcd < r8 ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
+  rank = lid % ntq;
+  bh = lid / ntq;
+}
+
 // Workgroup id -> logical id such that consecutive logical ids run on one XCD
 // (the hardware deals workgroup ids to the 8 XCDs round-robin).
 __device__ __forceinline__ int xcd_grouped_id(int bid, int nwg) {

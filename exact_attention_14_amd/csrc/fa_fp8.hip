@@ -295,7 +295,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
                     const uint8_t* __restrict__ V8, const float* __restrict__ SQ,
                     const float* __restrict__ SK, const float* __restrict__ SV,
                     u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg,
-                    int nblk, float scale) {
+                    int hpx, int nblk, float scale) {
   using G = Geo8<D>;
   using CP = TileCopy8<D, NW>;
   constexpr int BR = 32 * NW;
@@ -311,9 +311,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const int lid = xcd_grouped_id(blockIdx.x, nwg);
-  const int qtr = lid % ntq;
-  const int bh = lid / ntq;
+  int bh, qtr;
+  tile_of_workgroup(blockIdx.x, nwg, ntq, CAUSAL ? hpx : 0, bh, qtr);
   const int qt = CAUSAL ? (ntq - 1 - qtr) : qtr;
   const size_t head = (size_t)bh * (size_t)N;
   const unsigned head_bytes = (unsigned)N * D;
@@ -528,9 +527,10 @@ hipError_t fwd_launch(const void* q8, const void* k8, const void* v8, const floa
   const long long nwg = (long long)ntq * B * H;
   if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
   const int nblk = (N + kBlock - 1) / kBlock;
+  const int hpx = ((long long)B * H) % 8 == 0 ? (int)(((long long)B * H) / 8) : 0;
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                      stream, (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8, sq, sk,
-                     sv, (u16*)o, lse, N, ntq, (int)nwg, nblk, scale);
+                     sv, (u16*)o, lse, N, ntq, (int)nwg, hpx, nblk, scale);
   return hipGetLastError();
 }
 

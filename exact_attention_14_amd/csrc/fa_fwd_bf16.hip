@@ -322,7 +322,7 @@ __device__ __forceinline__ float max_with_other_half(float x) {
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg, float scale) {
+    u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg, int hpx, float scale) {
   using G = Geo<D>;
   using CP = TileCopy<D, NW>;
   constexpr int BR = 32 * NW;
@@ -339,9 +339,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const int lid = xcd_grouped_id(blockIdx.x, nwg);
-  const int qtr = lid % ntq;
-  const int bh = lid / ntq;
+  int bh, qtr;
+  tile_of_workgroup(blockIdx.x, nwg, ntq, CAUSAL ? hpx : 0, bh, qtr);
   const int qt = CAUSAL ? (ntq - 1 - qtr) : qtr;
   const size_t head = (size_t)bh * (size_t)N;
   const unsigned head_bytes = (unsigned)N * D * 2u;
@@ -567,10 +566,12 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   const int ntq = (N + 32 * NW - 1) / (32 * NW);
   const long long nwg = (long long)ntq * B * H;
   if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
+  // Causal: whole heads per XCD, longest tiles first, when the heads split evenly.
+  const int hpx = ((long long)B * H) % 8 == 0 ? (int)(((long long)B * H) / 8) : 0;
   if (!v2) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)nwg), dim3(4 * 64), 0,
                        stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N, ntq,
-                       (int)nwg, scale);
+                       (int)nwg, hpx, scale);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((fwd_bf16_v2_kernel<D, CAUSAL, 4>), dim3((unsigned)nwg), dim3(4 * 64), 0,
