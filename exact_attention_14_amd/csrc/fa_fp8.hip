@@ -447,6 +447,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     }
     const float mb = 8.f - ((m_ref == -INFINITY) ? 0.f : m_ref);  // exponent offset
     // Stage A: scores of tile t+1; softmax of tile t -> P * 2^8 as e4m3.
+    __builtin_amdgcn_s_setprio(1);
     scores(kr, s_nxt);
     int pw[8];  // byte b = kb * 16 + v
 #pragma unroll
@@ -468,6 +469,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     }
     // Nothing moves across: keeps stage B's V fragments out of stage A.
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     const i32x8 pv = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
     // Stage B: P V of tile t and the row sums; then the next tile's row max.
 #pragma unroll

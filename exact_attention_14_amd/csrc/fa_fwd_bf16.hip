@@ -487,7 +487,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
       }
     };
     // Stage A: scores of tile t+1 on the matrix cores, first half of the
-    // softmax of tile t on the VALU.
+    // softmax of tile t on the VALU. A wave in this stage takes issue
+    // priority over the other workgroup's wave on its SIMD, which then fills
+    // the matrix-core gaps with its own stage (the pages' ping-pong of two
+    // warp groups, here between the two resident workgroups).
+    __builtin_amdgcn_s_setprio(1);
     scores(kr, s_nxt);
     softmax_half(0);
     // Issue order: K fragment reads run two MFMAs ahead; each MFMA is
@@ -501,6 +505,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
     }
     // Nothing moves across: keeps stage B's V fragments out of stage A.
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     // Stage B: P V of tile t and the second half of its softmax.
     pv(vr, 0, p[0]);
     softmax_half(1);
