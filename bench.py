@@ -39,12 +39,20 @@ def source_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def time_calls(fn, steps, warmup):
+def time_calls(fn, steps, warmup, min_warm_s=0.3):
     """Average duration (ms) of fn() over `steps` calls, HIP events on the
-    current stream (the stream the library launches on)."""
+    current stream (the stream the library launches on). The untimed warm-up
+    runs at least `warmup` calls and at least `min_warm_s` seconds: after the
+    idle spell of generating inputs on the host the GPU clock needs some tens
+    of milliseconds to ramp back up."""
     import torch
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < min_warm_s:
         fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -66,7 +74,7 @@ def extras(fa):
     import fa_inputs
     out = []
 
-    def run(name, B, H, N, d, causal, seed, dtype=fa.FA_BF16, steps=20):
+    def run(name, B, H, N, d, causal, seed, dtype=fa.FA_BF16, steps=100):
         q, k, v = device_qkv(B, H, N, d, seed)
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
@@ -100,17 +108,17 @@ def extras(fa):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     f = flops(B, H, N, d, False)
-    ms = time_calls(lambda: fa.fwd_fp8(q8, k8, v8, sq, sk, sv, out=o, lse=lse), 20, 3)
+    ms = time_calls(lambda: fa.fwd_fp8(q8, k8, v8, sq, sk, sv, out=o, lse=lse), 100, 3)
     out.append({"name": "fp8 kernel (fa_fwd_fp8)", "B": B, "H": H, "N": N, "d": d,
                 "causal": False, "dtype": "fp8_e4m3", "ms": round(ms, 4),
                 "tflops": round(f / (ms * 1e-3) / 1e12, 1),
                 "pct_peak": round(100 * f / (ms * 1e-3) / 1e12 / PEAK_FP8, 1)})
-    ms = time_calls(lambda: fa.fwd(q, k, v, dtype=fa.FA_FP8_E4M3, out=o, lse=lse), 20, 3)
+    ms = time_calls(lambda: fa.fwd(q, k, v, dtype=fa.FA_FP8_E4M3, out=o, lse=lse), 100, 3)
     out.append({"name": "fp8 end to end (fa_fwd, quantisation included)", "B": B, "H": H,
                 "N": N, "d": d, "causal": False, "dtype": "fp8_e4m3", "ms": round(ms, 4),
                 "tflops": round(f / (ms * 1e-3) / 1e12, 1),
                 "pct_peak": round(100 * f / (ms * 1e-3) / 1e12 / PEAK_FP8, 1)})
-    ms = time_calls(lambda: fa.quant_fp8(q, signs=signs, out=q8, scales=sq), 20, 3)
+    ms = time_calls(lambda: fa.quant_fp8(q, signs=signs, out=q8, scales=sq), 100, 3)
     nbytes = B * H * N * d * 3 + B * H * ((N + 127) // 128) * 4
     out.append({"name": "fp8 quantiser with rotation (fa_quant_fp8, one tensor)", "B": B, "H": H,
                 "N": N, "d": d, "ms": round(ms, 4),
@@ -161,8 +169,10 @@ def traffic_record():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # About 0.3 s each on the default workload: the warm-up covers the clock
+    # ramp after the host-side input generation.
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
