@@ -34,7 +34,6 @@
 //   * Workgroups are renumbered so that the query tiles of one (batch, head)
 //     run on one XCD (workgroups are dealt to the 8 XCDs round-robin), which
 //     keeps that head's K/V in one L2. Causal query tiles run longest first.
-#include <cstdlib>
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -83,23 +82,6 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
   return __builtin_bit_cast(bf16x8, c);
 }
 
-// Issue this wave's share of the direct-to-LDS copies of one K or V tile.
-template <int D, int NW>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile, int j0,
-                                          int wave, int lane) {
-  using G = Geo<D>;
-  constexpr int NI = G::CPRP / NW;  // 1 KiB wave copies per tile per wave
-  static_assert(NI >= 1 && G::CPRP % NW == 0, "tile split");
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int slot = (i * NW + wave) * 64 + lane;  // chunk slot in the tile
-    const int row = slot / G::CPRP;
-    const int c = (slot % G::CPRP) ^ swz<G::CPRP>(row);
-    const unsigned off = c < G::CPR ? ((unsigned)(j0 + row) * D + c * 8) * 2u : 0x80000000u;
-    copy16_to_lds(rs, tile + (i * NW + wave) * 1024, off);
-  }
-}
-
 // Byte offsets past any head buffer (head buffers are at most 2 GiB): loads
 // there return zeros without memory traffic. Chunk slots beyond the data
 // width (d = 96) use kPadOffset; whole tiles past the end use kOutOfRange.
@@ -125,186 +107,20 @@ struct TileCopy {
       off[i] = c < G::CPR ? (unsigned)(row * D + c * 8) * 2u : kPadOffset;
     }
   }
-  // Copy the tile starting at key row j0 into `tile` (zeros if !valid).
+  // Copy i (0 <= i < NI) of the tile starting at key row j0 into `tile`
+  // (zeros if !valid).
+  __device__ __forceinline__ void issue_one(int i, i32x4 rs, char* tile, int j0, int wave,
+                                            bool valid) const {
+    const unsigned base = valid ? (unsigned)j0 * D * 2u : kOutOfRange;
+    copy16_to_lds_asm(rs, tile + (i * NW + wave) * 1024, off[i] + base);
+  }
+  // All NI copies of the tile, back to back.
   __device__ __forceinline__ void issue(i32x4 rs, char* tile, int j0, int wave,
                                         bool valid = true) const {
-    const unsigned base = valid ? (unsigned)j0 * D * 2u : kOutOfRange;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      copy16_to_lds_asm(rs, tile + (i * NW + wave) * 1024, off[i] + base);
+    for (int i = 0; i < NI; ++i) issue_one(i, rs, tile, j0, wave, valid);
   }
 };
-
-template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void fwd_bf16_v2_kernel(
-    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg, float scale) {
-  using G = Geo<D>;
-  constexpr int BR = 32 * NW;
-  // One LDS object per (stage, tensor): with the loop unrolled by two every
-  // read and every in-flight copy names a distinct object, so the compiler
-  // need not wait for the next tile's copies before reading the current one.
-  __shared__ __attribute__((aligned(1024))) char ks0[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char vs0[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char ks1[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char vs1[G::TILEB];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
-
-  // Workgroup id -> logical id with the tiles of one head on one XCD.
-  const int lid = xcd_grouped_id(blockIdx.x, nwg);
-  const int qtr = lid % ntq;
-  const int bh = lid / ntq;
-  const int qt = CAUSAL ? (ntq - 1 - qtr) : qtr;
-  const size_t head = (size_t)bh * (size_t)N;
-  const unsigned head_bytes = (unsigned)N * D * 2u;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head * D, head_bytes);
-
-  const int q0w = qt * BR + wave * 32;  // first query of this wave
-  const int qi = q0w + l32;             // this lane's query
-  const int q_last = min(N, qt * BR + BR) - 1;
-  const int ntiles = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
-
-  load_tile<D, NW>(rk, ks0, 0, wave, lane);
-  load_tile<D, NW>(rv, vs0, 0, wave, lane);
-
-  bf16x8 qreg[G::NK];
-#pragma unroll
-  for (int kk = 0; kk < G::NK; ++kk) {
-    const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-        rq, (unsigned)(qi * D + kk * 16 + half * 8) * 2u, 0, 0);
-    qreg[kk] = __builtin_bit_cast(bf16x8, w);
-  }
-
-  f32x16 oacc[G::NO];
-#pragma unroll
-  for (int i = 0; i < G::NO; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
-  float m_ref = -INFINITY;  // reference maximum (raw scores q.k) of O and l
-  float l_run = 0.f;        // this lane's half of the row sum
-  const float c = scale * kLog2e;
-
-  // Per-lane LDS byte offsets inside a tile.
-  const int krow = l32;                                   // + kb*32
-  const int kswz = swz<G::CPRP>(krow);
-  const int g16 = lane >> 4, i16 = lane & 15;             // tr16 lane group
-  const int vrow = 4 * half + (i16 >> 2);                 // + kb*32 + a*16 + r*8
-  const int vcol = (g16 & 1) * 2 + ((i16 & 3) >> 1);      // + blk*4 (chunk)
-  const int vbyte = (i16 & 1) * 8;
-
-  // One K/V tile: kt/vt hold tile t, kn/vn receive tile t+1.
-  auto step = [&](const char* kt, const char* vt, char* kn, char* vn, int t) {
-    // This wave's copies of tile t have landed (vmcnt counts LDS-DMA copies);
-    // after the barrier every wave's have, and the other stage is free.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      load_tile<D, NW>(rk, kn, (t + 1) * kBC, wave, lane);
-      load_tile<D, NW>(rv, vn, (t + 1) * kBC, wave, lane);
-    }
-    const int j0 = t * kBC;
-    if (CAUSAL && j0 > q0w + 31) return;  // every key after every query of this wave
-
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < G::NK; ++kk) {
-        const int chunk = (2 * kk + half) ^ kswz;
-        const bf16x8 a =
-            *(const bf16x8*)(kt + (kb * 32 + krow) * G::ROWB + chunk * 16);
-        acc = mfma32(a, qreg[kk], acc);
-      }
-      s[kb] = acc;
-    }
-
-    const bool need_mask = (j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > q0w);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = j0 + kb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-          if (key >= N || (CAUSAL && key > qi)) s[kb][v] = -INFINITY;
-        }
-    }
-
-    float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = (kb == 0 ? 2 : 0); v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = fmaxf(mx, xor32(mx));
-    // Move the reference when a row maximum exceeds it by more than 2^8 (or
-    // on the first keys a row sees); all lanes of the wave move together.
-    if (__any((mx - m_ref) * c > kLazyLog2)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < G::NO; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
-      m_ref = m_new;
-    }
-    const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
-    float lsum = 0.f;
-    bf16x8 p[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = fast_exp2(fmaf(s[kb][v], c, -mc));
-        lsum += e;
-        p[kb][v / 8][v % 8] = (__bf16)e;
-      }
-    l_run += lsum;
-
-#pragma unroll
-    for (int i = 0; i < G::NO; ++i)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int row0 = kb * 32 + a * 16 + vrow;           // read r = 0
-          const int row1 = row0 + 8;                          // read r = 1
-          const int ch = i * 4 + vcol;
-          const char* lo = vt + row0 * G::ROWB + ((ch ^ swz<G::CPRP>(row0)) * 16) + vbyte;
-          const char* hi = vt + row1 * G::ROWB + ((ch ^ swz<G::CPRP>(row1)) * 16) + vbyte;
-          oacc[i] = mfma32(tr_pair(lo, hi), p[kb][a], oacc[i]);
-        }
-    };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(ks0, vs0, ks1, vs1, t);
-    if (t + 1 < ntiles) step(ks1, vs1, ks0, vs0, t + 1);
-  }
-
-  const float l_tot = l_run + xor32(l_run);
-  const float inv = 1.f / l_tot;
-  if (qi < N) {
-    u16* orow = O + (head + qi) * D;
-#pragma unroll
-    for (int i = 0; i < G::NO; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 w;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[i][4 * g + x] * inv);
-        *(bf16x4*)(orow + i * 32 + 8 * g + 4 * half) = w;
-      }
-    if (LSE != nullptr && half == 0) LSE[head + qi] = m_ref * scale + __logf(l_tot);
-  }
-}
 
 // Exchange-and-max with the lane 32 positions away (v_permlane32_swap).
 __device__ __forceinline__ float max_with_other_half(float x) {
@@ -315,7 +131,7 @@ __device__ __forceinline__ float max_with_other_half(float x) {
 
 // Software-pipelined kernel: while the softmax of tile t runs on the VALU,
 // the scores of tile t+1 are already being formed on the matrix cores, and
-// the P V products of tile t overlap the second half of its softmax (QbitAI
+// the P V products of tile t overlap the row maximum of tile t+1 (QbitAI
 // article: two-stage GEMM-softmax pipelining, S_cur / S_next). K is copied
 // one tile further ahead than V through two-stage LDS rings; the copies are
 // issued as assembly so that only the kernel's own waits order them.
@@ -433,15 +249,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
       for (int v = (kb == 0 ? 2 : 0); v < 16; ++v) a = fmaxf(a, s[kb][v]);
     return max_with_other_half(a);
   };
-  auto pv = [&](const char* vt, int kb, const bf16x8* p) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int i = 0; i < G::NO; ++i) {
-        const char* blk = vt + (kb * 32 + a * 16) * G::ROWB;
-        oacc[i] = mfma32(tr_pair(blk + voff[i][0], blk + voff[i][1]), p[a], oacc[i]);
-      }
-  };
 
   f32x16 s_cur[2], s_nxt[2];
   // K_0 has landed once at most the Q loads and the two younger copies (all
@@ -457,14 +264,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
   // to vl. The last tile forms scores of a tile T that are discarded.
   // MASK: whether the scores of tile t+1 may need masking (edge tiles only;
   // the steady-state loop runs without the branch).
+  // Where the softmax of tile t runs: all of it beside the scores of tile t+1
+  // (stage A), leaving stage B to the P V products and the row maximum of
+  // tile t+1; or, for d = 256, whose stages hold twice the matrix-core work,
+  // half in each stage with the row maximum after stage B.
+  constexpr bool SOFT_A = D <= 128;
+  // VALU instructions placed after each matrix-core instruction: about 100
+  // softmax instructions per tile spread over stage A's 2*NK products.
+  constexpr int VALU_A = SOFT_A ? (100 + 2 * G::NK - 1) / (2 * G::NK) : 4;
+  constexpr int VALU_B = SOFT_A ? 2 : 4;
   auto step = [&](auto mask_tag, const char* kr, const char* vr, char* kl, char* vl, int t) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // This wave's copies of K_{t+1} and V_t have landed; after the barrier
     // every wave's have, and the stages of K_t and V_{t-1} are free.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    cp.issue(rk, kl, (t + 2) * kBC, wave, t + 2 < T);
-    cp.issue(rv, vl, (t + 1) * kBC, wave, t + 1 < T);
     if (__any((mt - m_ref) * c > kLazyLog2)) {
       const float m_new = fmaxf(m_ref, mt);
       const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - m_new) * c);
@@ -486,43 +300,84 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
         p[kb][v / 8][v % 8] = (__bf16)e;
       }
     };
-    // Stage A: scores of tile t+1 on the matrix cores, first half of the
-    // softmax of tile t on the VALU. A wave in this stage takes issue
-    // priority over the other workgroup's wave on its SIMD, which then fills
-    // the matrix-core gaps with its own stage (the pages' ping-pong of two
-    // warp groups, here between the two resident workgroups).
+    // Stage A: scores of tile t+1 on the matrix cores, softmax of tile t on
+    // the VALU. A wave in this stage takes issue priority over the other
+    // workgroup's wave on its SIMD, which then fills the matrix-core gaps
+    // with its own stage (the pages' ping-pong of two warp groups, here
+    // between the two resident workgroups). The NI copies of K_{t+2} are
+    // spread over the stage: issued back to back, the copies of all waves of
+    // a CU fill the texture unit's queues and stall the issuing waves.
     __builtin_amdgcn_s_setprio(1);
-    scores(kr, s_nxt);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s_nxt[kb][v] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < G::NK; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(kr + kb * 32 * G::ROWB + koff[kk]);
+        s_nxt[kb] = mfma32(a, qreg[kk], s_nxt[kb]);
+      }
+#pragma unroll
+      for (int ci = kk * CP::NI / G::NK; ci < (kk + 1) * CP::NI / G::NK; ++ci)
+        cp.issue_one(ci, rk, kl, (t + 2) * kBC, wave, t + 2 < T);
+    }
     softmax_half(0);
+    if constexpr (SOFT_A) softmax_half(1);
     // Issue order: K fragment reads run two MFMAs ahead; each MFMA is
-    // followed by four VALU/transcendental instructions of the softmax.
+    // followed by VALU_A VALU/transcendental instructions of the softmax.
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
 #pragma unroll
     for (int i = 0; i < 2 * G::NK; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU_A, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
     // Nothing moves across: keeps stage B's V fragments out of stage A.
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    // Stage B: P V of tile t and the second half of its softmax.
-    pv(vr, 0, p[0]);
-    softmax_half(1);
-    pv(vr, 1, p[1]);
+    // Stage B: P V of tile t, with the copies of V_{t+1} spread over it.
+    float mt_next = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < G::NO; ++i) {
+          const char* blk = vr + (kb * 32 + a * 16) * G::ROWB;
+          oacc[i] = mfma32(tr_pair(blk + voff[i][0], blk + voff[i][1]), p[kb][a], oacc[i]);
+          const int slot = (kb * 2 + a) * G::NO + i;
+#pragma unroll
+          for (int ci = slot * CP::NI / (4 * G::NO); ci < (slot + 1) * CP::NI / (4 * G::NO); ++ci)
+            cp.issue_one(ci, rv, vl, (t + 1) * kBC, wave, t + 1 < T);
+        }
+      if (kb == 0) {
+        if constexpr (SOFT_A) {
+          // Tile t+1's scores are complete: mask them and take their row
+          // maximum while the matrix cores work on P V.
+          if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
+          mt_next = rowmax(s_nxt);
+        } else {
+          softmax_half(1);
+        }
+      }
+    }
     l_run += lsum;
-    // Issue order: V fragment reads run two MFMAs ahead; each MFMA is
-    // followed by four VALU/transcendental instructions.
+    // Issue order: V fragment reads run two MFMAs ahead.
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
     for (int i = 0; i < 4 * G::NO; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU_B, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
-    mt = rowmax(s_nxt);
+    if constexpr (!SOFT_A) {
+      if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
+      mt_next = rowmax(s_nxt);
+    }
+    mt = mt_next;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
   };
@@ -562,26 +417,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int N, float scale, hipStream_t stream) {
-  static const bool use_v2 = [] {
-    const char* e = std::getenv("FA_BF16_KERNEL");
-    return e != nullptr && e[0] == 'v' && e[1] == '2';
-  }();
-  const bool v2 = use_v2;
-  const int NW = 4;
+  constexpr int NW = 4;
   const int ntq = (N + 32 * NW - 1) / (32 * NW);
   const long long nwg = (long long)ntq * B * H;
   if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
   // Causal: whole heads per XCD, longest tiles first, when the heads split evenly.
   const int hpx = ((long long)B * H) % 8 == 0 ? (int)(((long long)B * H) / 8) : 0;
-  if (!v2) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)nwg), dim3(4 * 64), 0,
-                       stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N, ntq,
-                       (int)nwg, hpx, scale);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL((fwd_bf16_v2_kernel<D, CAUSAL, 4>), dim3((unsigned)nwg), dim3(4 * 64), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                      stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N, ntq,
-                     (int)nwg, scale);
+                     (int)nwg, hpx, scale);
   return hipGetLastError();
 }
 
