@@ -284,9 +284,15 @@ __device__ __forceinline__ float max_other_half(float x) {
 // softmax of tile t, the matrix cores form the scores of tile t+1; the P V
 // products of tile t then overlap the row maxima of tile t+1.
 //   * P * 2^8 comes straight out of exp2 (8 is added to the exponent).
-//   * The row sum is taken by one more e4m3 product, ones(32 x 64) . P^T,
-//     whose every output row is sum_k P*2^8 for the lane's query: the sum of
-//     exactly the probabilities the P V product used.
+//   * V's block scales are folded into P instead of the accumulator: with
+//     sv_max the largest V block scale of the head, tile t's P is quantised
+//     as P * 2^8 * r_t, r_t = sv_t / sv_max <= 1 (one more term in the exp2
+//     argument), so the accumulator holds sum P V / sv_max and is rescaled
+//     only when the reference maximum moves.
+//   * The row sum is taken by one more e4m3 product per tile,
+//     ones(32 x 64) . P^T, whose every output row is sum_k P*2^8*r_t for the
+//     lane's query; divided by r_t it is the sum of exactly the
+//     probabilities the P V product used.
 //   * The reference maximum moves only when a row maximum exceeds it by more
 //     than 0.75 (log2 units), so P * 2^8 <= 2^8.75 = 430 stays within e4m3.
 template <int D, bool CAUSAL, int NW>
@@ -348,11 +354,18 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   for (int i = 0; i < G::NO; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
-  f32x16 lacc;  // every element: sum of P * 2^8 (only element 0 is read)
+  f32x16 zero16;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) lacc[v] = 0.f;
+  for (int v = 0; v < 16; ++v) zero16[v] = 0.f;
+  float l_run = 0.f;        // sum of P * 2^8 over the tiles so far
   float m_ref = -INFINITY;  // reference maximum, log2 units of scale * q.k
-  float sv_cur = 1.f;       // V scale the accumulator is expressed in
+  // Largest V block scale of the head (scales are positive; a non-positive
+  // or missing maximum leaves the fold at ratio 1).
+  float sv_max = 0.f;
+  for (int b = lane; b < nblk; b += 64) sv_max = fmaxf(sv_max, svh[b]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sv_max = fmaxf(sv_max, __shfl_xor(sv_max, o));
+  if (!(sv_max > 0.f)) sv_max = 1.f;
   const float c = scale * kLog2e;
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
@@ -432,20 +445,21 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     const int j0 = t * kBC;
     const float cs = c * sq * skh[min(j0, N - 1) / kBlock];  // raw MFMA result -> log2 units
     const float sv_t = svh[min(j0, N - 1) / kBlock];
+    const float r = sv_t > 0.f ? sv_t / sv_max : 1.f;  // V-scale fold of this tile
+    const float inv_r = sv_t > 0.f ? sv_max / sv_t : 1.f;
     const float mx = mt * cs;
-    if (__any(mx - m_ref > kLazy) || sv_t != sv_cur) {
+    if (__any(mx - m_ref > kLazy)) {
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m_new);
-      const float f = alpha * (sv_cur / sv_t);
-      lacc[0] *= alpha;
+      l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < G::NO; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[i][v] *= f;
+        for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
       m_ref = m_new;
-      sv_cur = sv_t;
     }
-    const float mb = 8.f - ((m_ref == -INFINITY) ? 0.f : m_ref);  // exponent offset
+    // exponent offset: 2^8 headroom, the reference maximum and the V fold
+    const float mb = 8.f - ((m_ref == -INFINITY) ? 0.f : m_ref) + __log2f(r);
     // Stage A: scores of tile t+1; softmax of tile t -> P * 2^8 as e4m3.
     __builtin_amdgcn_s_setprio(1);
     scores(kr, s_nxt);
@@ -482,9 +496,10 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
       const i32x8 a = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       oacc[i] = mfma8(a, pv, oacc[i]);
     }
-    lacc = mfma8(ones, pv, lacc);
+    const f32x16 lt = mfma8(ones, pv, zero16);
     if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
     mt = rowmax(s_nxt);
+    l_run = fmaf(lt[0], inv_r, l_run);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
   };
@@ -502,8 +517,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // no copy lands after the exit
 
-  const float l_tot = lacc[0];  // sum of P * 2^8
-  const float inv = sv_cur / l_tot;
+  const float l_tot = l_run;  // sum of P * 2^8
+  const float inv = sv_max / l_tot;
   if (qi < N) {
     u16* orow = O + (head + qi) * D;
 #pragma unroll

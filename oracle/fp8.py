@@ -122,19 +122,25 @@ def dequantize(codes, scales, block=BLOCK):
 
 
 def fp8_attention_emulate(q_codes, k_codes, v_codes, sq, sk, sv, causal, scale,
-                          p_scale=256.0, block=BLOCK, round_p=True):
+                          p_scale=256.0, block=BLOCK, round_p=True, v_fold=True):
     """Attention on dequantised FP8 operands with P rounded to e4m3.
 
     A prediction of the FP8 kernel's error, not a definition of the method:
     S = scale * Qd Kd^T from the dequantised (and, if rotated, rotated) Q, K;
-    P = exp(S - rowmax); P is rounded to e4m3 after multiplying by p_scale
-    (the FP8 product P V is taken in e4m3, QbitAI article, FP8 section); the
-    row sum is taken over the unrounded P in high precision; O = Pq Vd / sum.
+    P = exp(S - rowmax); the product P V is taken in e4m3 (QbitAI article,
+    FP8 section), so P is rounded to e4m3 after multiplying by p_scale and,
+    with v_fold, by r_j = (V scale of key j's block) / (largest V block scale
+    of the (batch, head)): the kernel applies V's block scales to P rather
+    than to its accumulator. The row sum is taken over the same rounded
+    values divided by p_scale * r_j, i.e. over the probabilities the product
+    used; O = sum_j Pq_j Vd_j / sum_j Pq_j. Without rounding (round_p=False)
+    this is exact attention on the dequantised operands whatever the scales.
     """
     qd = dequantize(q_codes, sq, block)
     kd = dequantize(k_codes, sk, block)
     vd = dequantize(v_codes, sv, block)
     B, H, N, d = qd.shape
+    sv64 = np.asarray(sv, dtype=np.float64)
     o = np.empty_like(vd)
     for b in range(B):
         for h in range(H):
@@ -143,10 +149,14 @@ def fp8_attention_emulate(q_codes, k_codes, v_codes, sq, sk, sv, causal, scale,
                 s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
             m = s.max(axis=1, keepdims=True)
             p = np.exp(s - m)
-            z = p.sum(axis=1, keepdims=True)
             if round_p:
-                pq = e4m3_decode(e4m3_encode(np.minimum(p * p_scale, E4M3_MAX))) / p_scale
+                if v_fold:
+                    r = np.repeat(sv64[b, h] / sv64[b, h].max(), block)[:N][None, :]
+                else:
+                    r = np.ones((1, N))
+                f = p_scale * r
+                pq = e4m3_decode(e4m3_encode(np.minimum(p * f, E4M3_MAX))) / f
             else:
                 pq = p
-            o[b, h] = (pq @ vd[b, h]) / z
+            o[b, h] = (pq @ vd[b, h]) / pq.sum(axis=1, keepdims=True)
     return o

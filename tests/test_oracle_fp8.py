@@ -125,3 +125,29 @@ def test_emulator_reduces_to_exact_attention():
         o_round = fp8.fp8_attention_emulate(*codes, ones, ones, ones, causal, 0.5)
         rel = np.linalg.norm(o_round - o_ref) / np.linalg.norm(o_ref)
         assert 0 < rel < 0.05
+
+
+def test_emulator_v_fold_invariants():
+    """The V-scale fold only moves where P is rounded: with equal block
+    scales it is the identity, and without rounding the emulator is exact
+    attention on the dequantised operands for any positive block scales."""
+    B, H, N, d = 1, 2, 300, 64
+    g = fa_inputs.make_qkv(B, H, N, d, 16, "outlier_replace")
+    qc, sq = fp8.quantize(g.q)
+    kc, sk = fp8.quantize(g.k)
+    vc, _ = fp8.quantize(g.v)
+    equal = np.full((B, H, 3), 2.0 ** -5, dtype=np.float32)
+    a = fp8.fp8_attention_emulate(qc, kc, vc, sq, sk, equal, False, 0.125, v_fold=True)
+    b = fp8.fp8_attention_emulate(qc, kc, vc, sq, sk, equal, False, 0.125, v_fold=False)
+    np.testing.assert_array_equal(a, b)
+    rng = np.random.default_rng(17)
+    sv = (2.0 ** rng.uniform(-8, -4, (B, H, 3))).astype(np.float32)
+    vals = [fp8.dequantize(c, s_) for c, s_ in ((qc, sq), (kc, sk), (vc, sv))]
+    for causal in (False, True):
+        o_ref, _ = attention(*vals, causal, 0.125)
+        o = fp8.fp8_attention_emulate(qc, kc, vc, sq, sk, sv, causal, 0.125, round_p=False)
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+        o_fold = fp8.fp8_attention_emulate(qc, kc, vc, sq, sk, sv, causal, 0.125)
+        rel = np.linalg.norm(o_fold - o_ref) / np.linalg.norm(o_ref)
+        assert 0 < rel < 0.05
+
