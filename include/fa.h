@@ -113,12 +113,18 @@ int fa_quant_fp8(const void* x, void* x8, float* scales,
  * stays in FP32).
  *
  * q8, k8, v8 : e4m3fn [B, H, N, d] with block scales q_scale, k_scale,
- *              v_scale : float32 [B, H, ceil(N/128)] as fa_quant_fp8 writes.
+ *              v_scale : float32 [B, H, ceil(N/128)] as fa_quant_fp8 writes
+ *              (positive; a non-positive V scale yields finite but
+ *              meaningless rows).
  * o : bf16 [B, H, N, d]; lse : float32 [B, H, N] or NULL; d : 64, 128, 256.
- * The probabilities P are multiplied by 256 and rounded to e4m3 for the P V
- * product; the row sum is the float32 accumulation of those same rounded
- * values (taken on the matrix cores), so O is normalised by the weights it
- * was formed with.
+ * The probabilities P of a key tile are multiplied by 256 * r, r = (V scale
+ * of the tile's block) / (largest V block scale of the (b, h)) <= 1, and
+ * rounded to e4m3 for the P V product; the row sum is the float32
+ * accumulation of those same rounded values divided by r (taken on the
+ * matrix cores), so O is normalised by the weights it was formed with.
+ * Where one head's V block scales differ by more than about 2^8, the P of
+ * the small-scale blocks fall into e4m3's subnormal range and lose relative
+ * precision.
  * Validation order as fa_fwd (null scale arrays -> INVALID_ARG).
  */
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
