@@ -261,7 +261,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
 
   // Tile t: S_t is in s_cur with its row max in mt; K_{t+1} (kr) and V_t (vr)
   // are in LDS once every wave passed the barrier; K_{t+2} goes to kl, V_{t+1}
-  // to vl. The last tile forms scores of a tile T that are discarded.
+  // to vl. The last step (t = T-1) only finishes tile t.
   // MASK: whether the scores of tile t+1 may need masking (edge tiles only;
   // the steady-state loop runs without the branch).
   // Where the softmax of tile t runs: all of it beside the scores of tile t+1
@@ -273,8 +273,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
   // softmax instructions per tile spread over stage A's 2*NK products.
   constexpr int VALU_A = SOFT_A ? (100 + 2 * G::NK - 1) / (2 * G::NK) : 4;
   constexpr int VALU_B = SOFT_A ? 2 : 4;
-  auto step = [&](auto mask_tag, const char* kr, const char* vr, char* kl, char* vl, int t) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // KIND: 0 = steady state (tile t+1 needs no mask), 1 = tile t+1 may need
+  // masking, 2 = last tile (t = T-1): there is no tile t+1 to score or copy.
+  auto step = [&](auto kind_tag, const char* kr, const char* vr, char* kl, char* vl, int t) {
+    constexpr int KIND = decltype(kind_tag)::value;
+    constexpr bool MASK = KIND == 1;
+    constexpr bool LAST = KIND == 2;
     // This wave's copies of K_{t+1} and V_t have landed; after the barrier
     // every wave's have, and the stages of K_t and V_{t-1} are free.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -308,31 +312,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
     // spread over the stage: issued back to back, the copies of all waves of
     // a CU fill the texture unit's queues and stall the issuing waves.
     __builtin_amdgcn_s_setprio(1);
+    if constexpr (!LAST) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s_nxt[kb][v] = 0.f;
+        for (int v = 0; v < 16; ++v) s_nxt[kb][v] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < G::NK; ++kk) {
+      for (int kk = 0; kk < G::NK; ++kk) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(kr + kb * 32 * G::ROWB + koff[kk]);
-        s_nxt[kb] = mfma32(a, qreg[kk], s_nxt[kb]);
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = *(const bf16x8*)(kr + kb * 32 * G::ROWB + koff[kk]);
+          s_nxt[kb] = mfma32(a, qreg[kk], s_nxt[kb]);
+        }
+#pragma unroll
+        for (int ci = kk * CP::NI / G::NK; ci < (kk + 1) * CP::NI / G::NK; ++ci)
+          cp.issue_one(ci, rk, kl, (t + 2) * kBC, wave, t + 2 < T);
       }
-#pragma unroll
-      for (int ci = kk * CP::NI / G::NK; ci < (kk + 1) * CP::NI / G::NK; ++ci)
-        cp.issue_one(ci, rk, kl, (t + 2) * kBC, wave, t + 2 < T);
     }
     softmax_half(0);
     if constexpr (SOFT_A) softmax_half(1);
     // Issue order: K fragment reads run two MFMAs ahead; each MFMA is
     // followed by VALU_A VALU/transcendental instructions of the softmax.
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    if constexpr (!LAST) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * G::NK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU_A, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      for (int i = 0; i < 2 * G::NK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU_A, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
     }
     // Nothing moves across: keeps stage B's V fragments out of stage A.
     __builtin_amdgcn_sched_barrier(0);
@@ -348,12 +356,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
           const char* blk = vr + (kb * 32 + a * 16) * G::ROWB;
           oacc[i] = mfma32(tr_pair(blk + voff[i][0], blk + voff[i][1]), p[kb][a], oacc[i]);
           const int slot = (kb * 2 + a) * G::NO + i;
+          if constexpr (!LAST) {
 #pragma unroll
-          for (int ci = slot * CP::NI / (4 * G::NO); ci < (slot + 1) * CP::NI / (4 * G::NO); ++ci)
-            cp.issue_one(ci, rv, vl, (t + 1) * kBC, wave, t + 1 < T);
+            for (int ci = slot * CP::NI / (4 * G::NO); ci < (slot + 1) * CP::NI / (4 * G::NO); ++ci)
+              cp.issue_one(ci, rv, vl, (t + 1) * kBC, wave, t + 1 < T);
+          }
         }
       if (kb == 0) {
-        if constexpr (SOFT_A) {
+        if constexpr (LAST) {
+          if constexpr (!SOFT_A) softmax_half(1);
+        } else if constexpr (SOFT_A) {
           // Tile t+1's scores are complete: mask them and take their row
           // maximum while the matrix cores work on P V.
           if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
@@ -373,27 +385,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!SOFT_A) {
+    if constexpr (!SOFT_A && !LAST) {
       if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
       mt_next = rowmax(s_nxt);
     }
-    mt = mt_next;
+    if constexpr (!LAST) {
+      mt = mt_next;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+    }
   };
 
   // Tiles j < J need no mask for any wave: every key of them precedes the
   // workgroup's first query (causal) and lies inside the sequence.
   const int J = CAUSAL ? min(N / kBC, (qt * BR + 1) / kBC) : N / kBC;
+  using Steady = std::integral_constant<int, 0>;
+  using Masked = std::integral_constant<int, 1>;
+  using Last = std::integral_constant<int, 2>;
   int t = 0;
   for (; t + 2 < J; t += 2) {  // steps whose next tile (t+1, t+2) is unmasked
-    step(std::false_type{}, ks1, vs0, ks0, vs1, t);
-    step(std::false_type{}, ks0, vs1, ks1, vs0, t + 1);
+    step(Steady{}, ks1, vs0, ks0, vs1, t);
+    step(Steady{}, ks0, vs1, ks1, vs0, t + 1);
   }
-  for (; t < T; t += 2) {  // t is even here: stage parity stays static
-    step(std::true_type{}, ks1, vs0, ks0, vs1, t);
-    if (t + 1 < T) step(std::true_type{}, ks0, vs1, ks1, vs0, t + 1);
+  for (; t + 2 < T; t += 2) {  // t is even here: stage parity stays static
+    step(Masked{}, ks1, vs0, ks0, vs1, t);
+    step(Masked{}, ks0, vs1, ks1, vs0, t + 1);
   }
+  if (t + 1 < T) {  // two tiles left
+    step(Masked{}, ks1, vs0, ks0, vs1, t);
+    ++t;
+  }
+  // The last step reads only V_t; one call site with the stage chosen at run
+  // time (two static-parity copies of the step raise register pressure into
+  // spills).
+  step(Last{}, ks0, (t & 1) ? vs1 : vs0, ks1, vs0, t);
   // No copy may land in LDS after the workgroup exits.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
