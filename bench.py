@@ -30,6 +30,15 @@ KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_14_amd", "csrc", "fa_fwd_bf1
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_B4H16N2048d128.json")
 
 
+PEAK_HBM = 8e12      # B/s, MI355X published
+RIDGE_BF16 = PEAK_BF16 * 1e12 / PEAK_HBM  # flop per byte where the two rooflines meet
+
+
+def algorithmic_bytes(B, H, N, d, e_in):
+    """Q, K, V read once (e_in bytes per element), O written in bf16, LSE in fp32."""
+    return B * H * N * (3 * d * e_in + 2 * d + 4)
+
+
 def flops(B, H, N, d, causal):
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
@@ -82,10 +91,14 @@ def extras(fa):
                         steps, 3)
         tf = flops(B, H, N, d, causal) / (ms * 1e-3) / 1e12
         peak = PEAK_BF16 if dtype == fa.FA_BF16 else PEAK_FP8
+        gbps = algorithmic_bytes(B, H, N, d, 2) / (ms * 1e-3) / 1e9
         out.append({"name": name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
                     "dtype": "bf16" if dtype == fa.FA_BF16 else "fp8_e4m3",
                     "ms": round(ms, 4), "tflops": round(tf, 1),
-                    "pct_peak": round(100 * tf / peak, 1)})
+                    "pct_peak": round(100 * tf / peak, 1),
+                    "gbps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / (PEAK_HBM / 1e9), 1),
+                    "bound": "hbm" if flops(B, H, N, d, causal) / algorithmic_bytes(B, H, N, d, 2)
+                             < RIDGE_BF16 else "mfma"})
         del q, k, v, o, lse
 
     run("mid causal", 4, 16, 2048, 128, True, fa_inputs.SEEDS["mid"])

@@ -236,7 +236,6 @@ __device__ __forceinline__ void load_tile8(__amdgpu_buffer_rsrc_t rs, char* tile
   }
 }
 
-typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 __device__ __forceinline__ i32x2 tr8(const char* p) {
@@ -434,14 +433,18 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   mask(s_cur, 0);
   float mt = rowmax(s_cur);  // raw row max of the tile about to be processed
 
-  // MASK: whether the scores of tile t+1 may need masking (edge tiles only;
-  // the steady-state loop runs without the branch).
-  auto step = [&](auto mask_tag, const char* kr, const char* vr, char* kl, char* vl, int t) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // KIND: 0 = steady state (tile t+1 needs no mask), 1 = tile t+1 may need
+  // masking, 2 = last tile (t = T-1): there is no tile t+1 to score or copy.
+  auto step = [&](auto kind_tag, const char* kr, const char* vr, char* kl, char* vl, int t) {
+    constexpr int KIND = decltype(kind_tag)::value;
+    constexpr bool MASK = KIND == 1;
+    constexpr bool LAST = KIND == 2;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // K_{t+1} and V_t landed
     __syncthreads();
-    cp.issue(rk, kl, (t + 2) * kBC, wave, t + 2 < T);
-    cp.issue(rv, vl, (t + 1) * kBC, wave, t + 1 < T);
+    if constexpr (!LAST) {
+      cp.issue(rk, kl, (t + 2) * kBC, wave, t + 2 < T);
+      cp.issue(rv, vl, (t + 1) * kBC, wave, t + 1 < T);
+    }
     const int j0 = t * kBC;
     const float cs = c * sq * skh[min(j0, N - 1) / kBlock];  // raw MFMA result -> log2 units
     const float sv_t = svh[min(j0, N - 1) / kBlock];
@@ -462,7 +465,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     const float mb = 8.f - ((m_ref == -INFINITY) ? 0.f : m_ref) + __log2f(r);
     // Stage A: scores of tile t+1; softmax of tile t -> P * 2^8 as e4m3.
     __builtin_amdgcn_s_setprio(1);
-    scores(kr, s_nxt);
+    if constexpr (!LAST) scores(kr, s_nxt);
     int pw[8];  // byte b = kb * 16 + v
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -474,12 +477,14 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
         const int w = cvt_pk_fp8<false>(e[0], e[1], 0);
         pw[kb * 4 + v4] = cvt_pk_fp8<true>(e[2], e[3], w);
       }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+    if constexpr (!LAST) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * G::NKS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 10, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      for (int i = 0; i < 2 * G::NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
     }
     // Nothing moves across: keeps stage B's V fragments out of stage A.
     __builtin_amdgcn_sched_barrier(0);
@@ -497,41 +502,41 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
       oacc[i] = mfma8(a, pv, oacc[i]);
     }
     const f32x16 lt = mfma8(ones, pv, zero16);
-    if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
-    mt = rowmax(s_nxt);
     l_run = fmaf(lt[0], inv_r, l_run);
+    if constexpr (!LAST) {
+      if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
+      mt = rowmax(s_nxt);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+    }
   };
   // Tiles j < J need no mask for any wave: every key of them precedes the
   // workgroup's first query (causal) and lies inside the sequence.
   const int J = CAUSAL ? min(N / kBC, (qt * BR + 1) / kBC) : N / kBC;
+  using Steady = std::integral_constant<int, 0>;
+  using Masked = std::integral_constant<int, 1>;
+  using Last = std::integral_constant<int, 2>;
   int t = 0;
   for (; t + 2 < J; t += 2) {  // steps whose next tile (t+1, t+2) is unmasked
-    step(std::false_type{}, ks1, vs0, ks0, vs1, t);
-    step(std::false_type{}, ks0, vs1, ks1, vs0, t + 1);
+    step(Steady{}, ks1, vs0, ks0, vs1, t);
+    step(Steady{}, ks0, vs1, ks1, vs0, t + 1);
   }
-  for (; t < T; t += 2) {  // t is even here: stage parity stays static
-    step(std::true_type{}, ks1, vs0, ks0, vs1, t);
-    if (t + 1 < T) step(std::true_type{}, ks0, vs1, ks1, vs0, t + 1);
+  for (; t + 2 < T; t += 2) {  // t is even here: stage parity stays static
+    step(Masked{}, ks1, vs0, ks0, vs1, t);
+    step(Masked{}, ks0, vs1, ks1, vs0, t + 1);
   }
+  if (t + 1 < T) {  // two tiles left
+    step(Masked{}, ks1, vs0, ks0, vs1, t);
+    ++t;
+  }
+  // The last step only finishes tile t (reads V_t); one call site with the
+  // stage chosen at run time.
+  step(Last{}, ks0, (t & 1) ? vs1 : vs0, ks1, (t & 1) ? vs0 : vs1, t);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // no copy lands after the exit
 
   const float l_tot = l_run;  // sum of P * 2^8
-  const float inv = sv_max / l_tot;
-  if (qi < N) {
-    u16* orow = O + (head + qi) * D;
-#pragma unroll
-    for (int i = 0; i < G::NO; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 w;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[i][4 * g + x] * inv);
-        *(bf16x4*)(orow + i * 32 + 8 * g + 4 * half) = w;
-      }
-    if (LSE != nullptr && half == 0) LSE[head + qi] = (m_ref + __log2f(l_tot) - 8.f) * kLn2;
-  }
+  store_o_lse<D>(O, LSE, head, N, qi, half, oacc, sv_max / l_tot,
+                 (m_ref + __log2f(l_tot) - 8.f) * kLn2);
 }
 
 template <int D, bool CAUSAL>

@@ -376,8 +376,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
       }
     }
     l_run += lsum;
-    // Issue order: V fragment reads run two MFMAs ahead.
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+    // Issue order: V fragment reads run three MFMAs ahead (two ahead
+    // measured 1-3% slower).
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
 #pragma unroll
     for (int i = 0; i < 4 * G::NO; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -423,20 +424,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   const float l_tot = l_run + xor32(l_run);
-  const float inv = 1.f / l_tot;
-  if (qi < N) {
-    u16* orow = O + (head + qi) * D;
-#pragma unroll
-    for (int i = 0; i < G::NO; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 w;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[i][4 * g + x] * inv);
-        *(bf16x4*)(orow + i * 32 + 8 * g + 4 * half) = w;
-      }
-    if (LSE != nullptr && half == 0) LSE[head + qi] = m_ref * scale + __logf(l_tot);
-  }
+  store_o_lse<D>(O, LSE, head, N, qi, half, oacc, 1.f / l_tot, m_ref * scale + __logf(l_tot));
 }
 
 template <int D, bool CAUSAL>

@@ -1,0 +1,77 @@
+"""Checks on the compiler's gfx950 output for the forward kernels (CPU only:
+hipcc cross-compiles to assembly text, nothing runs).
+
+No matrix-core instruction may be issued inside an exec-masked region. The
+32x32 products combine operands from all 64 lanes; run under a partial exec
+mask (after the compiler moved the last tile's products into a branch that
+only some lanes take) they gave wrong outputs. The kernels' epilogues are
+branch-free for this reason, and this test keeps it so.
+"""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_attention_14_amd import build as fa_build
+
+KERNELS = ("fa_fwd_bf16.hip", "fa_fp8.hip")
+
+
+def _hipcc():
+    try:
+        return fa_build.hipcc()
+    except RuntimeError:
+        return None
+
+
+def device_asm(src, out_dir):
+    out = os.path.join(out_dir, src + ".s")
+    cmd = [_hipcc(), *fa_build.COMMON, *fa_build.DEVICE_FLAGS, "--cuda-device-only", "-S",
+           os.path.join(fa_build.CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return open(out).read().split("\n")
+
+
+def mfma_under_exec_mask(lines):
+    """{kernel: count} of MFMAs between an exec save (s_and_saveexec /
+    s_andn2_saveexec) and the restore of exec, per forward kernel."""
+    bad, kernels, kern, masked = {}, [], None, False
+    for line in lines:
+        m = re.match(r"^(_Z\w*fwd_\w*kernel\w*):", line)
+        if m:
+            kern, masked = m.group(1), False
+            kernels.append(kern)
+            continue
+        if kern is None:
+            continue
+        s = line.strip()
+        if s.startswith(".Lfunc_end"):
+            kern = None
+        elif s.startswith(("s_and_saveexec", "s_andn2_saveexec")):
+            masked = True
+        elif re.match(r"s_(or|mov)_b64 exec", s):
+            masked = False
+        elif s.startswith("v_mfma") and masked:
+            bad[kern] = bad.get(kern, 0) + 1
+    return kernels, bad
+
+
+def test_detector_flags_a_masked_mfma():
+    text = ["_ZN2fa3fwd_x_kernelE:", "\ts_and_saveexec_b64 s[0:1], vcc",
+            "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], 0",
+            "\ts_or_b64 exec, exec, s[0:1]", "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], 0",
+            ".Lfunc_end0:"]
+    kernels, bad = mfma_under_exec_mask(text)
+    assert kernels == ["_ZN2fa3fwd_x_kernelE"] and bad == {"_ZN2fa3fwd_x_kernelE": 1}
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+@pytest.mark.parametrize("src", KERNELS)
+def test_no_mfma_under_partial_exec(src, tmp_path):
+    kernels, bad = mfma_under_exec_mask(device_asm(src, str(tmp_path)))
+    assert len(kernels) >= 6, kernels
+    assert bad == {}, f"MFMAs inside exec-masked regions: {bad}"
