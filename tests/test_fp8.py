@@ -105,6 +105,30 @@ def test_fwd_fp8_vs_emulator_and_exact(lib, d, causal):
     assert np.all(np.isfinite(lse_gpu))
 
 
+@pytest.mark.parametrize("N", [1, 17, 65, 129, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_ragged(lib, N, causal):
+    """Ragged sequence lengths: key-tile counts from 1 to 5 (both parities of
+    the last step's stage), partial last tiles, queries past N in the last
+    query tile."""
+    announce("fwd fp8 ragged", N, causal)
+    B, H, d = 1, 2, 64
+    g = fa_inputs.make_qkv(B, H, N, d, 730 + N, "outlier_replace")
+    qc, sq = fp8.quantize(g.q)
+    kc, sk = fp8.quantize(g.k)
+    vc, sv = fp8.quantize(g.v)
+    scale = 1.0 / math.sqrt(d)
+    o_gpu, lse_gpu = gpu_fwd_fp8(lib, (qc, kc, vc), (sq, sk, sv), causal)
+    o_emul = fp8.fp8_attention_emulate(qc, kc, vc, sq, sk, sv, causal, scale)
+    o_ref, lse_ref = attention(g.q, g.k, g.v, causal)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu))
+    e = rel_rmse(o_gpu, o_emul)
+    announce("  gpu-vs-emulator", e, "gpu-vs-exact", rel_rmse(o_gpu, o_ref),
+             "lse max abs", float(np.abs(lse_gpu - lse_ref).max()))
+    assert e <= 2e-2
+    assert rel_rmse(o_gpu, o_ref) <= 1.5 * FP8_REL_RMSE
+
+
 def test_fwd_fp8_causal_row0_closed_form(lib):
     announce("fwd fp8 causal row 0")
     g = fa_inputs.make_qkv(1, 2, 200, 128, 710)
