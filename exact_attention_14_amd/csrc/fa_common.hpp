@@ -112,6 +112,47 @@ __device__ __forceinline__ void store_o_lse(u16* O, float* LSE, size_t head, int
                                         half == 0 ? (unsigned)qi * 4u : 0x80000000u, 0, 0);
 }
 
+// The same epilogue with O staged through LDS. The wave writes its 32 rows x
+// D bf16 into `slot` (32 * 2D bytes, 16-byte aligned, not read by any other
+// wave any more), 16-byte chunk c of row r at chunk (c + r) mod D/8 so that
+// neither the 8-byte writes nor the 16-byte reads conflict; then each store
+// instruction writes 1 KiB of whole rows (16 contiguous bytes per lane)
+// instead of 8 bytes in each of 32 rows. q0w: first query of the wave.
+template <int D>
+__device__ __forceinline__ void store_o_lse_staged(u16* O, float* LSE, size_t head, int N,
+                                                   int q0w, int lane, const f32x16* oacc,
+                                                   float inv, float lse, char* slot) {
+  constexpr int NO = D / 32;
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int ROWB = D * 2;        // bytes per row
+  constexpr int NJ = 32 * ROWB / 1024;  // 1 KiB store instructions per wave
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < NO; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 w;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[i][4 * g + x] * inv);
+      const int chunk = (4 * i + g + l32) % CPR;
+      *(bf16x4*)(slot + l32 * ROWB + chunk * 16 + 8 * half) = w;
+    }
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head * D, (unsigned)N * D * 2u);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int flat = j * 1024 + lane * 16;
+    const int row = flat / ROWB, chunk = (flat % ROWB) / 16;
+    const i32x4 v = *(const i32x4*)(slot + row * ROWB + ((chunk + row) % CPR) * 16);
+    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (unsigned)((q0w + row) * ROWB + chunk * 16), 0,
+                                           0);
+  }
+  const __amdgpu_buffer_rsrc_t rl =
+      make_rsrc(LSE != nullptr ? (const void*)(LSE + head) : nullptr,
+                LSE != nullptr ? (unsigned)N * 4u : 0u);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(lse), rl,
+                                        half == 0 ? (unsigned)(q0w + l32) * 4u : 0x80000000u, 0, 0);
+}
+
 // Workgroup id -> (head, query-tile rank). Workgroup ids are dealt to the 8
 // XCDs round-robin. With hpx > 0 (B*H = 8*hpx heads) each XCD owns hpx whole
 // heads and starts its workgroups in rank order across them (rank 0 = the

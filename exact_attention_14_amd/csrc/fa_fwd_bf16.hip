@@ -423,8 +423,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
   // No copy may land in LDS after the workgroup exits.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
+  // The last step read no K stage and no copy is in flight: each wave stages
+  // its output rows in its own quarter of the two K stages.
+  static_assert(NW == 4 && 2 * 32 * 2 * D <= G::TILEB, "staging slots fit the K stages");
   const float l_tot = l_run + xor32(l_run);
-  store_o_lse<D>(O, LSE, head, N, qi, half, oacc, 1.f / l_tot, m_ref * scale + __logf(l_tot));
+  store_o_lse_staged<D>(O, LSE, head, N, q0w, lane, oacc, 1.f / l_tot,
+                        m_ref * scale + __logf(l_tot),
+                        (wave < 2 ? ks0 : ks1) + (wave & 1) * (32 * 2 * D));
 }
 
 template <int D, bool CAUSAL>
