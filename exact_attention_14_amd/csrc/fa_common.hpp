@@ -81,43 +81,20 @@ __device__ __forceinline__ void copy16_to_lds_asm(i32x4 rsrc, const void* lds, u
                : "memory", "m0");
 }
 
-// Epilogue of one wave: O^T (NO blocks of 32 output columns x 32 queries, lane
-// = query qi, element v = column 8*(v/4) + 4*half + v%4 of its block) scaled
-// by inv and rounded to bf16, and the lane's LSE. There is no branch on the
-// query bound: with a wave-divergent branch the compiler may move the last
-// matrix-core products into it, where they would run under a partial exec
-// mask. Rows past N fall outside the buffer range of the head's O rows and
-// are dropped by the hardware range check, as is the LSE store of the second
-// half-wave (and every LSE store when LSE is null).
-template <int D>
-__device__ __forceinline__ void store_o_lse(u16* O, float* LSE, size_t head, int N, int qi,
-                                            int half, const f32x16* oacc, float inv, float lse) {
-  constexpr int NO = D / 32;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head * D, (unsigned)N * D * 2u);
-#pragma unroll
-  for (int i = 0; i < NO; ++i)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 w;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[i][4 * g + x] * inv);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, w), ro,
-                                            (unsigned)(qi * D + i * 32 + 8 * g + 4 * half) * 2u,
-                                            0, 0);
-    }
-  const __amdgpu_buffer_rsrc_t rl =
-      make_rsrc(LSE != nullptr ? (const void*)(LSE + head) : nullptr,
-                LSE != nullptr ? (unsigned)N * 4u : 0u);
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(lse), rl,
-                                        half == 0 ? (unsigned)qi * 4u : 0x80000000u, 0, 0);
-}
-
-// The same epilogue with O staged through LDS. The wave writes its 32 rows x
-// D bf16 into `slot` (32 * 2D bytes, 16-byte aligned, not read by any other
-// wave any more), 16-byte chunk c of row r at chunk (c + r) mod D/8 so that
-// neither the 8-byte writes nor the 16-byte reads conflict; then each store
-// instruction writes 1 KiB of whole rows (16 contiguous bytes per lane)
-// instead of 8 bytes in each of 32 rows. q0w: first query of the wave.
+// Epilogue of one wave. O^T arrives as NO = D/32 blocks of 32 output columns
+// x 32 queries (lane = query q0w + lane % 32, element v = column
+// 8*(v/4) + 4*half + v%4 of its block); it is scaled by inv, rounded to bf16
+// and staged through LDS: the wave writes its 32 rows x D bf16 into `slot`
+// (32 * 2D bytes, 16-byte aligned, read by no other wave any more), 16-byte
+// chunk c of row r at chunk (c + r) mod D/8 so that neither the 8-byte
+// writes nor the 16-byte reads conflict; then each store instruction writes
+// 1 KiB of whole rows (16 contiguous bytes per lane) instead of 8 bytes in
+// each of 32 rows. There is no branch on the query bound: with a
+// wave-divergent branch the compiler may move the last matrix-core products
+// into it, where they would run under a partial exec mask. Rows past N fall
+// outside the buffer range of the head's O rows and are dropped by the
+// hardware range check, as is the LSE store of the second half-wave (and
+// every LSE store when LSE is null).
 template <int D>
 __device__ __forceinline__ void store_o_lse_staged(u16* O, float* LSE, size_t head, int N,
                                                    int q0w, int lane, const f32x16* oacc,

@@ -534,9 +534,16 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   step(Last{}, ks0, (t & 1) ? vs1 : vs0, ks1, (t & 1) ? vs0 : vs1, t);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // no copy lands after the exit
 
+  // Stage the output rows through LDS (whole-row stores): once every wave
+  // has finished the last step no stage is read and no copy is in flight,
+  // and wave w uses stage w (an e4m3 tile of 64 x d bytes holds a wave's 32
+  // rows of d bf16).
+  static_assert(NW == 4 && 32 * 2 * D <= G::TILEB, "staging slots fit the stages");
+  __syncthreads();
+  char* const slot = wave == 0 ? ks0 : wave == 1 ? ks1 : wave == 2 ? vs0 : vs1;
   const float l_tot = l_run;  // sum of P * 2^8
-  store_o_lse<D>(O, LSE, head, N, qi, half, oacc, sv_max / l_tot,
-                 (m_ref + __log2f(l_tot) - 8.f) * kLn2);
+  store_o_lse_staged<D>(O, LSE, head, N, q0w, lane, oacc, sv_max / l_tot,
+                        (m_ref + __log2f(l_tot) - 8.f) * kLn2, slot);
 }
 
 template <int D, bool CAUSAL>
