@@ -60,6 +60,22 @@ __device__ __forceinline__ int cvt_pk_fp8(float a, float b, int old) {
 // thread holds 8-element chunks; with rotation the CPR chunks of a row sit in
 // CPR consecutive lanes, so the Walsh-Hadamard butterflies run in registers
 // (strides 1, 2, 4) and across lanes (strides >= 8).
+// Value of v in lane (lane ^ m). m < 16 through DPP lane permutes within
+// 16-lane rows (xor 1 and 2: quad permutes; xor 4: half-row mirror then
+// quad xor 3; xor 8: row rotate by 8); wider strides through the LDS crossbar.
+__device__ __forceinline__ float lane_xor(float v, int m) {
+  const int b = __float_as_int(v);
+  switch (m) {
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false));
+    case 4:
+      return __int_as_float(__builtin_amdgcn_mov_dpp(
+          __builtin_amdgcn_mov_dpp(b, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF, false));
+    case 8: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, false));
+    default: return __shfl_xor(v, m);
+  }
+}
+
 template <int D, bool ROTATE, int MODE>
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const u16* __restrict__ X,
                                                         uint8_t* __restrict__ X8,
@@ -73,8 +89,10 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const u16* __restrict__ 
   const int blk = blockIdx.x % nblk;
   const size_t bh = blockIdx.x / nblk;
   const int row0 = blk * kBlock;
-  const size_t base = (bh * (size_t)N + row0) * D;
-  const int nrows = min(kBlock, N - row0);
+  // Buffer resources over the head's rows: loads past row N return zeros and
+  // stores there are dropped, so the ragged last block needs no branch.
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + bh * (size_t)N * D, (unsigned)N * D * 2u);
+  const __amdgpu_buffer_rsrc_t rx8 = make_rsrc(X8 + bh * (size_t)N * D, (unsigned)N * D);
 
   float x[NC][8];
   float amax = 0.f;
@@ -82,8 +100,8 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const u16* __restrict__ 
   for (int k = 0; k < NC; ++k) {
     const int cid = k * 256 + tid;
     const int row = cid / CPR, ch = cid % CPR;
-    uint4 w = {0u, 0u, 0u, 0u};
-    if (row < nrows) w = *(const uint4*)(X + base + (size_t)row * D + ch * 8);
+    const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+        rx, (unsigned)((row0 + row) * D + ch * 8) * 2u, 0, 0);
     const u16* e = (const u16*)&w;
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[k][j] = __uint_as_float((unsigned)e[j] << 16);
@@ -100,15 +118,13 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const u16* __restrict__ 
             x[k][j] = a + b;
             x[k][j + s] = a - b;
           }
-      // strides 8 .. D/2 across the lanes holding one row
+      // strides 8 .. D/2 across the lanes holding one row: the lane with the
+      // bit m clear keeps x + other, the one with it set other - x.
 #pragma unroll
       for (int m = 1; m < CPR; m <<= 1) {
-        const bool upper = (tid & m) != 0;
+        const float sgn = (tid & m) ? -1.f : 1.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float other = __shfl_xor(x[k][j], m);
-          x[k][j] = upper ? other - x[k][j] : x[k][j] + other;
-        }
+        for (int j = 0; j < 8; ++j) x[k][j] = fmaf(sgn, x[k][j], lane_xor(x[k][j], m));
       }
     }
 #pragma unroll
@@ -127,18 +143,20 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const u16* __restrict__ 
   }
   if constexpr (MODE == kGivenAmax) amax = scales[sidx];
   const float s = amax > 0.f ? amax / kE4m3Max : 1.f;
+  const float inv_s = 1.f / s;  // the scale is applied through its float32 reciprocal
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int cid = k * 256 + tid;
     const int row = cid / CPR, ch = cid % CPR;
     float t[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = fminf(fmaxf(x[k][j] / s, -kE4m3Max), kE4m3Max);
+    for (int j = 0; j < 8; ++j) t[j] = fminf(fmaxf(x[k][j] * inv_s, -kE4m3Max), kE4m3Max);
     int lo = cvt_pk_fp8<false>(t[0], t[1], 0);
     lo = cvt_pk_fp8<true>(t[2], t[3], lo);
     int hi = cvt_pk_fp8<false>(t[4], t[5], 0);
     hi = cvt_pk_fp8<true>(t[6], t[7], hi);
-    if (row < nrows) *(uint2*)(X8 + base + (size_t)row * D + ch * 8) = make_uint2(lo, hi);
+    const i32x2 packed = {lo, hi};
+    __builtin_amdgcn_raw_buffer_store_b64(packed, rx8, (unsigned)((row0 + row) * D + ch * 8), 0, 0);
   }
   if constexpr (MODE == kGivenAmax) __syncthreads();  // every thread has read scales[sidx]
   if (tid == 0) scales[sidx] = ROTATE ? s * rsqrt_d : s;

@@ -95,7 +95,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *          never V.
  * Quantisation: y = x diag(signs) H_d (float32; y = x without rotation),
  * s = amax|y| / 448 over the block (float32; 1 for an all-zero block),
- * code = round-to-nearest-even e4m3(clamp(y / s, +-448)); the stored scale is
+ * code = round-to-nearest-even e4m3(clamp(y * float32(1/s), +-448)); the stored scale is
  * s, or s * (1/sqrt(d)) with rotation.
  * Validation order: null x/x8/scales -> INVALID_ARG; B, H or N < 1 ->
  * INVALID_ARG; d not in {64, 96, 128, 256}, or signs given and d not a power

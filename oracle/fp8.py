@@ -24,9 +24,10 @@ Readings where the pages are silent (each also listed in the design notes):
     usually exact in float32); the 1/sqrt(d) is folded into the stored scale.
   * the quantisation decision is taken in float32, as the kernel takes it:
     amax over the block of |float32(y)|, s = float32(amax) / 448 (IEEE float32
-    division; s = 1 for an all-zero block), t = float32(y) / s (IEEE float32
-    division), clamped to [-448, 448], rounded to the nearest e4m3 value with
-    ties to even. The stored scale is s, or float32(s * float32(1/sqrt(d)))
+    division; s = 1 for an all-zero block), t = float32(y) * float32(1 / s)
+    (the block's scale applied as a multiplication by its correctly rounded
+    float32 reciprocal), clamped to [-448, 448], rounded to the nearest e4m3
+    value with ties to even. The stored scale is s, or float32(s * float32(1/sqrt(d)))
     when rotated; dequantised value = e4m3 value * stored scale.
 """
 from __future__ import annotations
@@ -103,8 +104,9 @@ def quantize(x, per_tensor=False, signs=None, block=BLOCK):
     if per_tensor:
         amax[...] = amax.max()
     s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    s_rows = np.repeat(s, block, axis=2)[:, :, :N, None]          # scale per row
-    t = (y32 / s_rows).astype(np.float32)
+    inv = (np.float32(1.0) / s).astype(np.float32)                # float32 reciprocal
+    inv_rows = np.repeat(inv, block, axis=2)[:, :, :N, None]      # per row
+    t = (y32 * inv_rows).astype(np.float32)
     t = np.clip(t, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     codes = e4m3_encode(t)
     if signs is not None:
