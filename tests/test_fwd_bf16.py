@@ -150,3 +150,31 @@ def test_lse_optional_and_scale(lib):
     o_gpu = fa_inputs.bf16_bits_to_f64(fa_inputs.bf16_tensor_to_bits(o))
     ok, st = bf16_gate(o_gpu, o_ref)
     assert ok, st
+
+
+def _random_cases(count, seed):
+    """Valid random configurations from a fixed generator: head size, mask,
+    batch, heads, a sequence length with ragged tails, and the scale."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        d = int(rng.choice([64, 96, 128, 256]))
+        N = int(rng.integers(1, 700))
+        cases.append((i, int(rng.integers(1, 3)), int(rng.integers(1, 4)), N, d, bool(rng.integers(2)),
+                      float(rng.choice([0.5, 1.0, 2.0])) / math.sqrt(d), 900 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(12, 77), ids=lambda c: f"r{c[0]}-N{c[3]}-d{c[4]}")
+def test_random_shapes(lib, case):
+    _, B, H, N, d, causal, scale, seed = case
+    announce("random", B, H, N, d, "causal" if causal else "noncausal", "scale", scale, "seed", seed)
+    g = fa_inputs.make_qkv(B, H, N, d, seed)
+    o_gpu, lse_gpu = run_bf16(lib, g, causal, scale=scale)
+    o_ref, lse_ref = attention(g.q, g.k, g.v, causal, scale)
+    ok, st = bf16_gate(o_gpu, o_ref)
+    lse_err = float(np.abs(lse_gpu - lse_ref).max())
+    announce("  stats", st, "lse_max_abs", lse_err)
+    assert ok, st
+    assert lse_err <= LSE_MAX_ABS
+
