@@ -31,6 +31,13 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
+// Maximum of x and the x of the lane 32 positions away (v_permlane32_swap).
+__device__ __forceinline__ float max_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32);
@@ -38,6 +45,19 @@ __device__ __forceinline__ float xor32(float x) {
 
 // s_waitcnt immediate: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
+
+// s_waitcnt immediate for vmcnt = n (n < 64), expcnt and lgkmcnt at maxima.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Buffer byte offset past any head buffer (head buffers are below 2 GiB):
+// loads and copies there return zeros and stores are dropped, with no memory
+// traffic.
+constexpr unsigned kOutOfRange = 0x80000000u;
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier masks.
+constexpr int kSchedValu = 0x002 | 0x400;  // VALU and transcendental
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 // Raw buffer resource (gfx9 family dword 3: 32-bit data format). Loads at
 // byte offsets >= `bytes` return zeros without touching memory.
@@ -47,13 +67,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, unsig
                                            kBufferFlags);
 }
 
-// 16-byte copy HBM -> LDS for each lane; the wave writes 1 KiB contiguous at
-// `lds` (wave-uniform) + 16 * lane.
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, void* lds,
-                                              unsigned byte_off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds,
-                                           16, byte_off, 0, 0, 0);
-}
 
 // Buffer resource as four dwords for inline assembly (base, stride 0,
 // num_records = bytes, gfx9 dword 3).
@@ -127,7 +140,7 @@ __device__ __forceinline__ void store_o_lse_staged(u16* O, float* LSE, size_t he
       make_rsrc(LSE != nullptr ? (const void*)(LSE + head) : nullptr,
                 LSE != nullptr ? (unsigned)N * 4u : 0u);
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(lse), rl,
-                                        half == 0 ? (unsigned)(q0w + l32) * 4u : 0x80000000u, 0, 0);
+                                        half == 0 ? (unsigned)(q0w + l32) * 4u : kOutOfRange, 0, 0);
 }
 
 // Workgroup id -> (head, query-tile rank). Workgroup ids are dealt to the 8
@@ -150,12 +163,5 @@ __device__ __forceinline__ void tile_of_workgroup(int bid, int nwg, int ntq, int
   bh = lid / ntq;
 }
 
-// Workgroup id -> logical id such that consecutive logical ids run on one XCD
-// (the hardware deals workgroup ids to the 8 XCDs round-robin).
-__device__ __forceinline__ int xcd_grouped_id(int bid, int nwg) {
-  const int q8 = nwg >> 3, r8 = nwg & 7;
-  const int xcd = bid & 7, loc = bid >> 3;
-  return xcd < r8 ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
-}
 
 }  // namespace fa

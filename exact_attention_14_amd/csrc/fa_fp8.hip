@@ -22,7 +22,6 @@ namespace {
 
 constexpr int kBlock = 128;      // rows per quantisation block
 constexpr float kE4m3Max = 448.f;
-constexpr float kPScale = 256.f; // P is rounded to e4m3 as P * 2^8
 
 // ----------------------------------------------------------------- signs ----
 
@@ -225,35 +224,6 @@ __device__ __forceinline__ int swz8(int row) {
   }
 }
 
-// Byte offset past any head buffer: copies there return zeros, no traffic.
-constexpr unsigned kOutOfRange8 = 0x80000000u;
-
-// s_waitcnt immediate for vmcnt = n (n < 64), expcnt and lgkmcnt at maxima.
-constexpr int waitcnt_vm8(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
-// Instruction classes of __builtin_amdgcn_sched_group_barrier masks.
-constexpr int kSchedValu = 0x002 | 0x400;
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-
-template <int D, int NW>
-__device__ __forceinline__ void load_tile8(__amdgpu_buffer_rsrc_t rs, char* tile, int j0,
-                                           int wave, int lane) {
-  using G = Geo8<D>;
-  constexpr int NCH = kBC * G::CPR;           // chunks per tile
-  constexpr int NI = (NCH + 64 * NW - 1) / (64 * NW);
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int w = i * NW + wave;              // 1 KiB wave copy index
-    if (w * 64 < NCH) {
-      const int slot = w * 64 + lane;
-      const int row = slot / G::CPR;
-      const int c = (slot % G::CPR) ^ swz8<D>(row);
-      copy16_to_lds(rs, tile + w * 1024, (unsigned)(j0 + row) * D + c * 16);
-    }
-  }
-}
-
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 __device__ __forceinline__ i32x2 tr8(const char* p) {
@@ -278,24 +248,18 @@ struct TileCopy8 {
       const int slot = (i * NW + wave) * 64 + lane;
       const int row = slot / G::CPR;
       const int c = (slot % G::CPR) ^ swz8<D>(row);
-      off[i] = slot < NCH ? (unsigned)(row * D + c * 16) : kOutOfRange8;
+      off[i] = slot < NCH ? (unsigned)(row * D + c * 16) : kOutOfRange;
     }
   }
   static_assert(NCH % (64 * NW) == 0, "every wave issues the same number of copies");
   __device__ __forceinline__ void issue(i32x4 rs, char* tile, int j0, int wave, bool valid) const {
-    const unsigned base = valid ? (unsigned)j0 * D : kOutOfRange8;
+    const unsigned base = valid ? (unsigned)j0 * D : kOutOfRange;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       copy16_to_lds_asm(rs, tile + (i * NW + wave) * 1024, off[i] + base);
   }
 };
 
-// Exchange-and-max with the lane 32 positions away (v_permlane32_swap).
-__device__ __forceinline__ float max_other_half(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 
 // Same software pipeline as the bf16 kernel: while the VALU runs the
 // softmax of tile t, the matrix cores form the scores of tile t+1; the P V
@@ -441,11 +405,11 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = (kb == 0 ? 2 : 0); v < 16; ++v) a = fmaxf(a, s[kb][v]);
-    return max_other_half(a);
+    return max_with_other_half(a);
   };
 
   f32x16 s_cur[2], s_nxt[2];
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm8(2 * G::NKS + 2 * CP::NI));  // K_0 landed
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * G::NKS + 2 * CP::NI));  // K_0 landed
   __syncthreads();
   scores(ks0, s_cur);
   mask(s_cur, 0);

@@ -44,10 +44,6 @@ namespace {
 
 constexpr int kBC = 64;          // keys per K/V tile
 constexpr float kLazyLog2 = 8.f; // rescale threshold, log2 units
-// Instruction classes of __builtin_amdgcn_sched_group_barrier masks.
-constexpr int kSchedValu = 0x002 | 0x400;  // VALU and transcendental
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
 
 template <int D>
 struct Geo {
@@ -82,14 +78,10 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
   return __builtin_bit_cast(bf16x8, c);
 }
 
-// Byte offsets past any head buffer (head buffers are at most 2 GiB): loads
-// there return zeros without memory traffic. Chunk slots beyond the data
-// width (d = 96) use kPadOffset; whole tiles past the end use kOutOfRange.
+// Byte offset for the chunk slots beyond the data width (d = 96): past any
+// head buffer (head buffers are at most 2 GiB), so copies there return zeros
+// without memory traffic.
 constexpr unsigned kPadOffset = 0x40000000u;
-constexpr unsigned kOutOfRange = 0x80000000u;
-
-// s_waitcnt immediate for vmcnt = n (n < 64), expcnt and lgkmcnt at maxima.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // Per-lane byte offsets (tile row 0) of this wave's share of a tile copy;
 // rows past the data width get an offset beyond any buffer (zero fill).
@@ -122,12 +114,6 @@ struct TileCopy {
   }
 };
 
-// Exchange-and-max with the lane 32 positions away (v_permlane32_swap).
-__device__ __forceinline__ float max_with_other_half(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 
 // Software-pipelined kernel: while the softmax of tile t runs on the VALU,
 // the scores of tile t+1 are already being formed on the matrix cores, and
