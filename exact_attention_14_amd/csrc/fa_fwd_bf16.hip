@@ -259,6 +259,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
   // softmax instructions per tile spread over stage A's 2*NK products.
   constexpr int VALU_A = SOFT_A ? (100 + 2 * G::NK - 1) / (2 * G::NK) : 4;
   constexpr int VALU_B = SOFT_A ? 2 : 4;
+  // LDS fragment reads run ahead of their MFMAs: at d <= 128 K fragments two
+  // MFMAs ahead and V fragments (two transposed reads each) three ahead (two
+  // ahead measured 1-3% slower); d = 256, one wave per SIMD with no other
+  // wave to fill the gaps, reads both four MFMAs ahead (+2 to +7%).
+  constexpr int RA_K = D == 256 ? 4 : 2;
+  constexpr int RA_V = D == 256 ? 8 : 6;
   // KIND: 0 = steady state (tile t+1 needs no mask), 1 = tile t+1 may need
   // masking, 2 = last tile (t = T-1): there is no tile t+1 to score or copy.
   auto step = [&](auto kind_tag, const char* kr, const char* vr, char* kl, char* vl, int t) {
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
     // Issue order: K fragment reads run two MFMAs ahead; each MFMA is
     // followed by VALU_A VALU/transcendental instructions of the softmax.
     if constexpr (!LAST) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RA_K, 0);
 #pragma unroll
       for (int i = 0; i < 2 * G::NK; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -362,9 +368,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 25
       }
     }
     l_run += lsum;
-    // Issue order: V fragment reads run three MFMAs ahead (two ahead
-    // measured 1-3% slower).
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+    // Issue order: V fragment reads run RA_V / 2 MFMAs ahead.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RA_V, 0);
 #pragma unroll
     for (int i = 0; i < 4 * G::NO; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
