@@ -10,6 +10,9 @@ Contents
   attention.py  exact softmax(scale * Q K^T) V and per-row log-sum-exp in
                 float64, materialising S and P (pinned: closed forms,
                 brute force, invariants, a library routine).
+  attention_grad.py  dQ, dK, dV of sum(dO * O) for the same attention, in
+                float64 (pinned: central finite differences, a library
+                routine's autograd, closed forms, invariants).
   fp8.py        e4m3fn encode/decode, per-block and per-tensor quantisation
                 with optional random-sign Hadamard rotation (pinned: a library
                 cast, the format's closed forms, H H^T = d I, rotation
@@ -20,4 +23,5 @@ Contents
                 exact attention up to the rounding of P).
 """
 from .attention import attention, attention_rows, attention_sampled  # noqa: F401
+from .attention_grad import attention_backward  # noqa: F401
 from . import fp8  # noqa: F401
