@@ -38,82 +38,12 @@
 
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
+#include "fa_tiles_bf16.hpp"
 
 namespace fa {
 namespace {
 
-constexpr int kBC = 64;          // keys per K/V tile
 constexpr float kLazyLog2 = 8.f; // rescale threshold, log2 units
-
-template <int D>
-struct Geo {
-  static constexpr int CPR = D / 8;                                  // 16-B chunks of data per row
-  static constexpr int CPRP = D == 64 ? 8 : (D == 256 ? 32 : 16);    // chunk slots per LDS row
-  static constexpr int ROWB = CPRP * 16;                             // bytes per LDS row
-  static constexpr int TILEB = kBC * ROWB;                           // one K or V tile
-  static constexpr int STAGEB = 2 * TILEB;                           // K + V
-  static constexpr int NK = D / 16;                                  // k-steps of S^T = K Q^T
-  static constexpr int NO = D / 32;                                  // 32-row blocks of O^T
-};
-
-// Chunk-slot XOR for LDS row `row`; see the design notes for the bank model.
-template <int CPRP>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (CPRP == 8) {
-    const int s = row >> 1;
-    return ((s & 1) << 2) | ((s >> 1) & 3);
-  } else {
-    return ((row & 3) << 2) | ((row >> 2) & 3);
-  }
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi);
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, c);
-}
-
-// Byte offset for the chunk slots beyond the data width (d = 96): past any
-// head buffer (head buffers are at most 2 GiB), so copies there return zeros
-// without memory traffic.
-constexpr unsigned kPadOffset = 0x40000000u;
-
-// Per-lane byte offsets (tile row 0) of this wave's share of a tile copy;
-// rows past the data width get an offset beyond any buffer (zero fill).
-template <int D, int NW>
-struct TileCopy {
-  static constexpr int NI = Geo<D>::CPRP / NW;
-  unsigned off[NI];
-  __device__ __forceinline__ TileCopy(int wave, int lane) {
-    using G = Geo<D>;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int slot = (i * NW + wave) * 64 + lane;
-      const int row = slot / G::CPRP;
-      const int c = (slot % G::CPRP) ^ swz<G::CPRP>(row);
-      off[i] = c < G::CPR ? (unsigned)(row * D + c * 8) * 2u : kPadOffset;
-    }
-  }
-  // Copy i (0 <= i < NI) of the tile starting at key row j0 into `tile`
-  // (zeros if !valid).
-  __device__ __forceinline__ void issue_one(int i, i32x4 rs, char* tile, int j0, int wave,
-                                            bool valid) const {
-    const unsigned base = valid ? (unsigned)j0 * D * 2u : kOutOfRange;
-    copy16_to_lds_asm(rs, tile + (i * NW + wave) * 1024, off[i] + base);
-  }
-  // All NI copies of the tile, back to back.
-  __device__ __forceinline__ void issue(i32x4 rs, char* tile, int j0, int wave,
-                                        bool valid = true) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) issue_one(i, rs, tile, j0, wave, valid);
-  }
-};
-
 
 // Software-pipelined kernel: while the softmax of tile t runs on the VALU,
 // the scores of tile t+1 are already being formed on the matrix cores, and
