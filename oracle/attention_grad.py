@@ -19,6 +19,13 @@ chain rule through the softmax, written out with nothing fused or reordered:
 
 The whole N x N matrices of one (batch, head) are formed; P comes from the
 row maximum subtracted before the exponential, as in the forward oracle.
+
+Optional `o`: the row term sum_k P_ik dP_ik equals sum_c dO_ic O_ic (the dot
+product of row i of dO with row i of O = P V). A backward pass that is handed
+the forward's stored output forms the term that second way, from the O it is
+given; passing that O here evaluates the same formula with the same term, so
+that the stored output's rounding is part of the reference rather than of the
+error. With the exact O both ways agree (pinned in the tests).
 """
 from __future__ import annotations
 
@@ -35,12 +42,15 @@ def _probabilities(q, k, causal, scale):
     return e / e.sum(axis=1, keepdims=True)
 
 
-def attention_backward(q, k, v, do, causal=False, scale=None):
+def attention_backward(q, k, v, do, causal=False, scale=None, o=None):
     """Gradients of sum(dO * attention(Q, K, V)) over [B, H, N, d] inputs.
 
     Returns (dq, dk, dv), float64 [B, H, N, d]. `scale` defaults to 1/sqrt(d).
+    With `o` ([B, H, N, d], a forward output), the row term is sum_c dO_ic O_ic.
     """
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    if o is not None:
+        o = np.asarray(o, dtype=np.float64)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / np.sqrt(d)
@@ -52,7 +62,11 @@ def attention_backward(q, k, v, do, causal=False, scale=None):
             p = _probabilities(q[b, h], k[b, h], causal, scale)
             dv[b, h] = p.T @ do[b, h]
             dp = do[b, h] @ v[b, h].T
-            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            if o is None:
+                row = (p * dp).sum(axis=1, keepdims=True)
+            else:
+                row = (do[b, h] * o[b, h]).sum(axis=1, keepdims=True)
+            ds = p * (dp - row)
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ q[b, h])
     return dq, dk, dv

@@ -101,3 +101,29 @@ def test_invariants(causal):
     dq2, dk2, dv2 = attention_backward(q, k + u, v, do, causal, 0.9)
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
         np.testing.assert_allclose(b, a, rtol=1e-9, atol=1e-11)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_term_from_forward_output(causal):
+    """With the exact forward output the row term sum_c dO_ic O_ic equals
+    sum_j P_ij dP_ij, so passing o changes nothing. Perturbing o by E shifts
+    the row term by e_i = sum_c dO_ic E_ic and dS_ij by -P_ij e_i: dV is
+    unchanged, dQ_i moves by -scale e_i (P K)_i with (P K)_i the forward
+    output for values K, and the dK rows' sum moves by -scale sum_i e_i Q_i
+    (rows of P sum to one)."""
+    B, H, N, d = 2, 2, 29, 7
+    q, k, v, do = (_rand((B, H, N, d), 600 + i) for i in range(4))
+    scale = 0.8
+    o, _ = attention(q, k, v, causal, scale)
+    base = attention_backward(q, k, v, do, causal, scale)
+    same = attention_backward(q, k, v, do, causal, scale, o=o)
+    for a, b in zip(base, same):
+        np.testing.assert_allclose(b, a, rtol=1e-10, atol=1e-12)
+    e_mat = 1e-3 * _rand((B, H, N, d), 610)
+    dq, dk, dv = attention_backward(q, k, v, do, causal, scale, o=o + e_mat)
+    e = (do * e_mat).sum(axis=3)                       # [B, H, N]
+    pk, _ = attention(q, k, k, causal, scale)
+    np.testing.assert_allclose(dv, base[2], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(dq - base[0], -scale * e[..., None] * pk, rtol=1e-8, atol=1e-13)
+    np.testing.assert_allclose((dk - base[1]).sum(axis=2), -scale * (e[..., None] * q).sum(axis=2),
+                               rtol=1e-8, atol=1e-13)
