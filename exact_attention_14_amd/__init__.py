@@ -1,4 +1,5 @@
-"""Python binding of libfa.so, the MI355X FlashAttention forward library.
+"""Python binding of libfa.so, the MI355X FlashAttention library (forward and
+backward passes).
 
 Argument marshalling only: tensors are checked, outputs are allocated with
 torch on the caller's device, and the C entry points of include/fa.h are called
@@ -26,7 +27,7 @@ FA_ERR_MISALIGNED = -3
 FA_ERR_HIP = -4
 FA_ERR_TOO_LARGE = -5
 
-EXPORTS = ("fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_status_string", "fa_version")
+EXPORTS = ("fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_bwd", "fa_status_string", "fa_version")
 
 
 class FAError(RuntimeError):
@@ -54,6 +55,8 @@ def _load():
     lib.fa_quant_fp8.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, fp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_bwd.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -154,6 +157,34 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = 
                         _stream(q8.device))
     _check(st, "fa_fwd_fp8")
     return o, lse
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
+        dq=None, dk=None, dv=None):
+    """Attention backward on bf16 [B, H, N, d] tensors; returns (dq, dk, dv).
+
+    o and lse are the forward's outputs for the same q, k, v, causal, scale;
+    do is the upstream gradient of o.
+    """
+    torch = _check_qkv(q, k, v, torch_bf16())
+    B, H, N, d = q.shape
+    for name, t in (("o", o), ("do", do)):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(q.shape) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like q")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on another device than q")
+    if lse is None or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) \
+            or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                    _ptr(dv), B, H, N, d, int(bool(causal)), float(scale), _stream(q.device))
+    _check(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def torch_bf16():

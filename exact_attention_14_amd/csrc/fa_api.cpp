@@ -23,6 +23,7 @@ bool log_enabled() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool bf16_dim_ok(int d) { return d == 64 || d == 96 || d == 128 || d == 256; }
+bool bwd_dim_ok(int d) { return d == 64 || d == 96 || d == 128; }
 bool fp8_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool pow2(int d) { return d > 0 && (d & (d - 1)) == 0; }
 
@@ -138,6 +139,35 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_sc
   return hip_status(fa::launch_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N,
                                        d, causal != 0, scale, static_cast<hipStream_t>(stream)),
                     "fwd_fp8 launch");
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+           int causal, float scale, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
+      dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (!bwd_dim_ok(d)) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  int st = sizes_check(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (log_enabled())
+    std::fprintf(stderr, "[fa] fa_bwd B=%d H=%d N=%d d=%d causal=%d scale=%g\n", B, H, N, d,
+                 causal, (double)scale);
+  // Stream-ordered scratch: the per-row D and -LSE*log2(e) terms.
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, 2 * (size_t)B * H * N * sizeof(float), s);
+  if (e != hipSuccess) return hip_status(e, "hipMallocAsync");
+  e = fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(ws), B, H, N,
+                          d, causal != 0, scale, s);
+  hipError_t ef = hipFreeAsync(ws, s);
+  if (e != hipSuccess) return hip_status(e, "bwd_bf16 launch");
+  return hip_status(ef, "hipFreeAsync");
 }
 
 const char* fa_status_string(int status) {

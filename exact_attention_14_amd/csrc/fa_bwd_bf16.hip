@@ -1,0 +1,400 @@
+// FlashAttention backward pass, bf16 inputs, fp32 accumulation, gfx950.
+//
+// What is computed (the gradients of sum(dO * O) for the forward pass of
+// fa_fwd_bf16.hip; the QbitAI FlashAttention-3 article times this backward
+// pass beside the forward): with P = softmax(scale * Q K^T) recomputed tile by
+// tile from the forward's per-row log-sum-exp (no running maximum is needed
+// on the way back),
+//   D_i  = sum_c dO_ic O_ic                (pre-pass, = sum_j P_ij dP_ij)
+//   dV   = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+//   dQ   = scale * dS K,  dK = scale * dS^T Q.
+// The N x N matrices never leave the chip. Two kernels share the work without
+// atomics (results are deterministic): one owns a tile of keys and sweeps the
+// query tiles for dK and dV, the other owns a tile of queries and sweeps the
+// key tiles for dQ; both recompute S and dP.
+//
+// gfx950 mapping (same building blocks as the forward kernel)
+//   * dK/dV: each lane owns one key. K and V stay in registers as the B
+//     operands of S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16); the
+//     outputs then hold, per lane, 16 queries of a 32-query block, which is
+//     exactly the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS, whose
+//     A operands are the Q and dO tiles read transposed from LDS
+//     (ds_read_b64_tr_b16). The per-query LSE and D are read per element.
+//   * dQ: each lane owns one query (the forward's layout): S^T = K Q^T and
+//     dP^T = V dO^T from the K and V tiles, then dQ^T += K^T dS^T with K read
+//     transposed; LSE and D are per-lane scalars.
+//   * Tiles of 64 rows move HBM -> LDS by direct-to-LDS copies into a
+//     two-stage ring (one tile of prefetch), with the forward's swizzle.
+//   * The gradients are stored with the forward's staged epilogue.
+#include <type_traits>
+
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+#include "fa_tiles_bf16.hpp"
+
+namespace fa {
+namespace {
+
+// --------------------------------------------------------------- pre-pass ---
+
+// Per-row terms of the backward pass, one thread per row r < rows:
+//   Dout[r]  = sum_c dO[r][c] * O[r][c]   (float32 sums of bf16 products)
+//   NLout[r] = -LSE[r] * log2(e)          (P = exp2(scale log2(e) S + NL))
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const u16* __restrict__ O,
+                                                       const u16* __restrict__ dO,
+                                                       const float* __restrict__ LSE,
+                                                       float* __restrict__ Dout,
+                                                       float* __restrict__ NLout, long long rows) {
+  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const uint4* o = (const uint4*)(O + r * D);
+  const uint4* g = (const uint4*)(dO + r * D);
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const uint4 a = o[c], b = g[c];
+    const u16* ea = (const u16*)&a;
+    const u16* eb = (const u16*)&b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc = fmaf(__uint_as_float((unsigned)ea[j] << 16), __uint_as_float((unsigned)eb[j] << 16),
+                 acc);
+  }
+  Dout[r] = acc;
+  NLout[r] = -LSE[r] * kLog2e;
+}
+
+// 4-byte HBM -> LDS copy per lane (lane l writes lds + 4 l), written as
+// assembly for the same reason as the 16-byte tile copies: the kernel's own
+// s_waitcnt decides when it is complete. `lds` must be wave-uniform.
+__device__ __forceinline__ void copy4_to_lds_asm(i32x4 rsrc, const void* lds, unsigned byte_off) {
+  const unsigned m0 = (unsigned)reinterpret_cast<unsigned long long>(
+      (const __attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(byte_off), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Offsets shared by both kernels: K-style row reads (lane = row l32 of a
+// 32-row block, 16-byte chunk 2*kk + half) and V-style transposed reads (the
+// forward's P V operand pattern), per lane, within a 64-row tile.
+template <int D>
+struct Offsets {
+  using G = Geo<D>;
+  int row[G::NK];
+  int tr[G::NO][2];
+  __device__ __forceinline__ Offsets(int lane) {
+    const int half = lane >> 5, l32 = lane & 31;
+    const int rs = swz<G::CPRP>(l32);
+#pragma unroll
+    for (int kk = 0; kk < G::NK; ++kk) row[kk] = l32 * G::ROWB + (((2 * kk + half) ^ rs) << 4);
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int vrow = 4 * half + (i16 >> 2);
+    const int vcol = (g16 & 1) * 2 + ((i16 & 3) >> 1);
+    const int vbyte = (i16 & 1) * 8;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int rr = vrow + 8 * r;
+      const int sw = swz<G::CPRP>(rr);
+#pragma unroll
+      for (int i = 0; i < G::NO; ++i) tr[i][r] = rr * G::ROWB + (((i * 4 + vcol) ^ sw) << 4) + vbyte;
+    }
+  }
+};
+
+// A 32 x 32 block of (tile rows of `tile` starting at block row rb*32) x
+// (the 32 lanes' own rows held in `reg`): acc = tile_rows . reg^T.
+template <int D>
+__device__ __forceinline__ f32x16 rows_times_reg(const char* tile, int rb, const Offsets<D>& off,
+                                                 const bf16x8* reg) {
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < Geo<D>::NK; ++kk) {
+    const bf16x8 a = *(const bf16x8*)(tile + rb * 32 * Geo<D>::ROWB + off.row[kk]);
+    acc = mfma32(a, reg[kk], acc);
+  }
+  return acc;
+}
+
+// acc[i] += tile^T (d block i x 64 rows) . b, with b[rb][a] the B operand of
+// rows rb*32 + a*16 .. +15 in the permuted order of the transposed reads.
+template <int D>
+__device__ __forceinline__ void tile_t_times(const char* tile, const Offsets<D>& off,
+                                             const bf16x8 (*b)[2], f32x16* acc) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < Geo<D>::NO; ++i) {
+        const char* blk = tile + (rb * 32 + a * 16) * Geo<D>::ROWB;
+        acc[i] = mfma32(tr_pair(blk + off.tr[i][0], blk + off.tr[i][1]), b[rb][a], acc[i]);
+      }
+}
+
+// Row fragments of the lane's own row (row < N, else zeros) as B operands.
+template <int D>
+__device__ __forceinline__ void load_own_rows(__amdgpu_buffer_rsrc_t r, int row, int half,
+                                              bf16x8* reg) {
+#pragma unroll
+  for (int kk = 0; kk < Geo<D>::NK; ++kk) {
+    const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+        r, (unsigned)(row * D + kk * 16 + half * 8) * 2u, 0, 0);
+    reg[kk] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV --
+
+// Workgroup: 4 waves x 32 keys = one 128-key tile of one (batch, head); it
+// sweeps the 64-query tiles that attend to it (causal: from its first key
+// on). Q, dO and the query tile's NL and D move HBM -> LDS one tile ahead.
+// Grid: B*H*ceil(N/128); causal key tiles run lowest index (most query
+// tiles) first.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const u16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
+    u16* __restrict__ dK, u16* __restrict__ dV, int N, int nkt, int nwg, int hpx, float scale) {
+  using G = Geo<D>;
+  using CP = TileCopy<D, 4>;
+  __shared__ __attribute__((aligned(1024))) char qs0[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char gs0[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char qs1[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char gs1[G::TILEB];
+  __shared__ __attribute__((aligned(16))) float rowt[2][2][kBC];  // [stage][NL, D][query]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  int bh, kt;
+  tile_of_workgroup(blockIdx.x, nwg, nkt, CAUSAL ? hpx : 0, bh, kt);
+  const size_t head = (size_t)bh * (size_t)N;
+  const unsigned head_bytes = (unsigned)N * D * 2u;
+  const i32x4 rq = make_rsrc_words(Q + head * D, head_bytes);
+  const i32x4 rg = make_rsrc_words(dO + head * D, head_bytes);
+  // Waves 0 and 1 copy the NL and D rows of a query tile; queries past N
+  // read as zeros (their products are masked).
+  const i32x4 rr = make_rsrc_words((wave == 0 ? NL : Dvec) + head, (unsigned)N * 4u);
+
+  const int k0w = kt * 128 + wave * 32;  // first key of the wave
+  const int kj = k0w + l32;              // the lane's key
+  const int u0 = CAUSAL ? (kt * 128) / kBC : 0;  // first query tile
+  const int U = (N + kBC - 1) / kBC;
+  const float c = scale * kLog2e;
+
+  const CP cp(wave, lane);
+  auto issue = [&](char* qn, char* gn, int st, int u) {
+    cp.issue(rq, qn, u * kBC, wave, true);
+    cp.issue(rg, gn, u * kBC, wave, true);
+    if (wave < 2) copy4_to_lds_asm(rr, rowt[st][wave], (unsigned)(u * kBC + lane) * 4u);
+  };
+  issue(qs0, gs0, 0, u0);
+  bf16x8 kreg[G::NK], vreg[G::NK];
+  load_own_rows<D>(make_rsrc(K + head * D, head_bytes), kj, half, kreg);
+  load_own_rows<D>(make_rsrc(V + head * D, head_bytes), kj, half, vreg);
+  const Offsets<D> off(lane);
+
+  f32x16 dk[G::NO], dv[G::NO];
+#pragma unroll
+  for (int i = 0; i < G::NO; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
+
+  // Query tile u (in stage st): Q_u in qc, dO_u in gc; tile u+1 goes to the
+  // other stage.
+  auto step = [&](const char* qc, const char* gc, char* qn, char* gn, int st, int u) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (u + 1 < U) issue(qn, gn, st ^ 1, u + 1);
+    const int q0 = u * kBC;
+    bf16x8 pb[2][2], sb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // NL and D of the 16 queries this lane holds in block qb: query
+      // qb*32 + 8*g + 4*half + x for element v = 4*g + x.
+      f32x4 nl4[4], d4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        nl4[g] = *(const f32x4*)&rowt[st][0][qb * 32 + 8 * g + 4 * half];
+        d4[g] = *(const f32x4*)&rowt[st][1][qb * 32 + 8 * g + 4 * half];
+      }
+      const f32x16 s = rows_times_reg<D>(qc, qb, off, kreg);   // S = Q K^T
+      const f32x16 dp = rows_times_reg<D>(gc, qb, off, vreg);  // dP = dO V^T
+      const bool edge = (q0 + qb * 32 + 32 > N) || (CAUSAL && k0w + 31 > q0 + qb * 32);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int q = q0 + qb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+        float p = fast_exp2(fmaf(s[v], c, nl4[v / 4][v % 4]));
+        if (edge && (q >= N || (CAUSAL && kj > q))) p = 0.f;
+        const float ds = p * (dp[v] - d4[v / 4][v % 4]);
+        pb[qb][v / 8][v % 8] = (__bf16)p;
+        sb[qb][v / 8][v % 8] = (__bf16)ds;
+      }
+    }
+    tile_t_times<D>(gc, off, pb, dv);  // dV^T += dO^T P
+    tile_t_times<D>(qc, off, sb, dk);  // dK^T += Q^T dS
+  };
+
+  int u = u0;
+  for (; u + 1 < U; u += 2) {
+    step(qs0, gs0, qs1, gs1, 0, u);
+    step(qs1, gs1, qs0, gs0, 1, u + 1);
+  }
+  if (u < U) step(qs0, gs0, qs1, gs1, 0, u);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();  // every wave is done with the tiles: they hold the staging slots
+  static_assert(2 * 32 * 2 * D <= G::TILEB, "two staging slots per tile");
+  char* const slot = (wave < 2 ? qs0 : qs1) + (wave & 1) * (32 * 2 * D);
+  store_o_lse_staged<D>(dK, nullptr, head, N, k0w, lane, dk, scale, 0.f, slot);
+  store_o_lse_staged<D>(dV, nullptr, head, N, k0w, lane, dv, 1.f, 0.f, slot);
+}
+
+// ---------------------------------------------------------------------- dQ --
+
+// Workgroup: 4 waves x 32 queries = one 128-query tile of one (batch, head);
+// it sweeps the 64-key tiles the queries attend to. Grid: B*H*ceil(N/128);
+// causal query tiles run longest first.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const u16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
+    u16* __restrict__ dQ, int N, int ntq, int nwg, int hpx, float scale) {
+  using G = Geo<D>;
+  using CP = TileCopy<D, 4>;
+  __shared__ __attribute__((aligned(1024))) char ks0[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vs0[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char ks1[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vs1[G::TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  int bh, qtr;
+  tile_of_workgroup(blockIdx.x, nwg, ntq, CAUSAL ? hpx : 0, bh, qtr);
+  const int qt = CAUSAL ? (ntq - 1 - qtr) : qtr;
+  const size_t head = (size_t)bh * (size_t)N;
+  const unsigned head_bytes = (unsigned)N * D * 2u;
+  const i32x4 rk = make_rsrc_words(K + head * D, head_bytes);
+  const i32x4 rv = make_rsrc_words(V + head * D, head_bytes);
+
+  const int q0w = qt * 128 + wave * 32;
+  const int qi = q0w + l32;
+  const int q_last = min(N, qt * 128 + 128) - 1;
+  const int T = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
+  const float c = scale * kLog2e;
+
+  const CP cp(wave, lane);
+  cp.issue(rk, ks0, 0, wave, true);
+  cp.issue(rv, vs0, 0, wave, true);
+  bf16x8 qreg[G::NK], greg[G::NK];
+  load_own_rows<D>(make_rsrc(Q + head * D, head_bytes), qi, half, qreg);
+  load_own_rows<D>(make_rsrc(dO + head * D, head_bytes), qi, half, greg);
+  // Queries past N read zeros (their rows are dropped at the store).
+  const float nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(NL + head, (unsigned)N * 4u), (unsigned)qi * 4u, 0, 0));
+  const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(Dvec + head, (unsigned)N * 4u), (unsigned)qi * 4u, 0, 0));
+  const Offsets<D> off(lane);
+
+  f32x16 dq[G::NO];
+#pragma unroll
+  for (int i = 0; i < G::NO; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dq[i][v] = 0.f;
+
+  // Key tile t: K_t in kc, V_t in vc; K_{t+1}, V_{t+1} go to kn, vn.
+  auto step = [&](const char* kc, const char* vc, char* kn, char* vn, int t) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (t + 1 < T) {
+      cp.issue(rk, kn, (t + 1) * kBC, wave, true);
+      cp.issue(rv, vn, (t + 1) * kBC, wave, true);
+    }
+    const int j0 = t * kBC;
+    const bool edge = (j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > q0w);
+    bf16x8 sb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x16 s = rows_times_reg<D>(kc, kb, off, qreg);   // S^T = K Q^T
+      const f32x16 dp = rows_times_reg<D>(vc, kb, off, greg);  // dP^T = V dO^T
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = j0 + kb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+        float p = fast_exp2(fmaf(s[v], c, nl));
+        if (edge && (key >= N || (CAUSAL && key > qi))) p = 0.f;
+        sb[kb][v / 8][v % 8] = (__bf16)(p * (dp[v] - dd));
+      }
+    }
+    tile_t_times<D>(kc, off, sb, dq);  // dQ^T += K^T dS^T
+  };
+
+  int t = 0;
+  for (; t + 1 < T; t += 2) {
+    step(ks0, vs0, ks1, vs1, t);
+    step(ks1, vs1, ks0, vs0, t + 1);
+  }
+  if (t < T) step(ks0, vs0, ks1, vs1, t);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();  // every wave is done with the tiles: they hold the staging slots
+  static_assert(2 * 32 * 2 * D <= G::TILEB, "two staging slots per tile");
+  char* const slot = (wave < 2 ? ks0 : ks1) + (wave & 1) * (32 * 2 * D);
+  store_o_lse_staged<D>(dQ, nullptr, head, N, q0w, lane, dq, scale, 0.f, slot);
+}
+
+template <int D, bool CAUSAL>
+hipError_t bwd_launch(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      float* ws, int B, int H, int N, float scale, hipStream_t stream) {
+  const long long rows = (long long)B * H * N;
+  float* const dvec = ws;
+  float* const nl = ws + rows;
+  hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                     stream, (const u16*)o, (const u16*)dout, lse, dvec, nl, rows);
+  const int nt = (N + 127) / 128;
+  const long long nwg = (long long)nt * B * H;
+  if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
+  const int hpx = ((long long)B * H) % 8 == 0 ? (int)(((long long)B * H) / 8) : 0;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream,
+                     (const u16*)q, (const u16*)k, (const u16*)v, (const u16*)dout,
+                     (const float*)nl, (const float*)dvec, (u16*)dk, (u16*)dv, N, nt, (int)nwg,
+                     hpx, scale);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream,
+                     (const u16*)q, (const u16*)k, (const u16*)v, (const u16*)dout,
+                     (const float*)nl, (const float*)dvec, (u16*)dq, N, nt, (int)nwg, hpx, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* ws, int B, int H, int N, int d, bool causal, float scale,
+                           hipStream_t stream) {
+#define FA_CASE(DD)                                                                          \
+  case DD:                                                                                   \
+    return causal ? bwd_launch<DD, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N,     \
+                                         scale, stream)                                     \
+                  : bwd_launch<DD, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N,    \
+                                          scale, stream);
+  switch (d) {
+    FA_CASE(64)
+    FA_CASE(96)
+    FA_CASE(128)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef FA_CASE
+}
+
+}  // namespace fa

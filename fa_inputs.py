@@ -17,6 +17,9 @@ Workloads (all synthetic; the pages measure on synthetic data themselves):
   * random signs in {-1, +1} for the random-sign Hadamard rotation used by
     incoherent processing (FlashAttention-3 (HE), section on FP8 with
     incoherent processing).
+  * an upstream gradient dO for the backward pass: iid N(0,1) entries of the
+    output's shape, rounded to bf16 (the pages give no distribution for it;
+    this is the plainest choice, the same as the inputs').
 """
 from __future__ import annotations
 
@@ -83,6 +86,13 @@ def make_qkv(B, H, N, d, seed, dist="normal") -> QKV:
     return QKV(B, H, N, d, seed, dist)
 
 
+def make_grad(B, H, N, d, seed):
+    """Upstream gradient dO [B, H, N, d]: (bf16 bit patterns, exact float64)."""
+    rng = np.random.default_rng(seed)
+    bits = bf16_bits(draw(rng, (B, H, N, d), "normal"))
+    return bits, bf16_bits_to_f64(bits)
+
+
 def random_signs(d: int, seed: int) -> np.ndarray:
     """d independent signs in {-1, +1} as float32."""
     rng = np.random.default_rng(seed)
@@ -110,4 +120,5 @@ SEEDS = {
     "dim_sweep_base": 400,   # + index of d in (64, 96, 128, 256)
     "fp8": 5,
     "fp8_signs": 55,
+    "grad_offset": 100000,   # dO seed = the Q/K/V seed + this offset
 }

@@ -1,5 +1,6 @@
 /*
- * fa.h - FlashAttention forward for AMD Instinct MI355X (gfx950), C ABI.
+ * fa.h - FlashAttention for AMD Instinct MI355X (gfx950), C ABI: the forward
+ * pass (bf16 and FP8) and the bf16 backward pass.
  *
  * The library computes exact scaled-dot-product attention
  *     O = softmax(scale * Q K^T) V,   LSE_i = log sum_j exp(scale * q_i . k_j)
@@ -131,6 +132,39 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
                const float* q_scale, const float* k_scale, const float* v_scale,
                void* o, float* lse, int B, int H, int N, int d, int causal,
                float scale, void* stream);
+
+/*
+ * fa_bwd - attention backward pass, bf16 (the pass the QbitAI
+ * FlashAttention-3 article times beside the forward in its benchmark
+ * section; its arithmetic is the chain rule through the softmax).
+ *
+ * For O = softmax(scale * Q K^T) V (causal mask as fa_fwd) and an upstream
+ * gradient dO, writes the gradients of sum(dO * O):
+ *     D_i = sum_c dO_ic O_ic,   P = exp(scale * Q K^T - LSE) (masked: 0)
+ *     dV = P^T dO,   dS = P * (dO V^T - D),
+ *     dQ = scale * dS K,   dK = scale * dS^T Q.
+ * P is recomputed tile by tile from the forward's LSE; no N x N matrix is
+ * stored. Each gradient row is written by exactly one workgroup (no atomics:
+ * results are bitwise reproducible run to run).
+ *
+ * q, k, v, o, dout : bf16 [B, H, N, d] (inputs; o and lse are what fa_fwd
+ *                    returned for the same q, k, v, causal and scale)
+ * lse              : float32 [B, H, N] (input, required)
+ * dq, dk, dv       : bf16 [B, H, N, d] (outputs; must not alias the inputs)
+ * d                : 64, 96 or 128
+ * Arithmetic: bf16 matrix-core products with float32 accumulation; P and dS
+ * are rounded to bf16 as operands of the second products; D is a float32 sum.
+ * Scratch: 2 * B*H*N floats, stream-ordered (hipMallocAsync/hipFreeAsync on
+ * `stream`).
+ * Validation order: null q/k/v/o/lse/dout/dq/dk/dv -> INVALID_ARG; B, H or
+ * N < 1 -> INVALID_ARG; d not in {64, 96, 128} -> UNSUPPORTED; scale not
+ * finite and > 0 -> INVALID_ARG; N*d > 2^30 or B*H >= 2^31 -> TOO_LARGE; a
+ * pointer not 16-byte aligned -> MISALIGNED; launch or scratch allocation
+ * error -> HIP.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, int causal, float scale, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

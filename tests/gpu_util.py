@@ -42,6 +42,47 @@ def bf16_gate(o_gpu, o_ref):
     return ok, stats
 
 
+# Backward gates, relative to the gradient's own size (see test_bwd_bf16.py).
+BWD_REL_MAX = 1e-2
+BWD_REL_RMSE = 5e-3
+# Absolute floor for gradients that vanish exactly (one key: dK = 0), where the
+# float32 sums of the kernel leave residues near 2^-24 of their terms.
+BWD_ABS_FLOOR = 1e-4
+
+
+def bwd_gate(g_gpu, g_ref):
+    """Returns (ok, stats) for one gradient tensor of the backward pass."""
+    err = np.abs(g_gpu - g_ref)
+    if err.size == 0:
+        return True, {}
+    scale_max = float(np.abs(g_ref).max())
+    norm = float(np.sqrt((g_ref ** 2).sum()))
+    allowed = BWD_REL_MAX * scale_max + half_ulp_bf16(g_ref) + BWD_ABS_FLOOR
+    stats = {
+        "max_abs": float(err.max()),
+        "ref_max": scale_max,
+        "rel_max": float(err.max()) / scale_max if scale_max > 0 else float(err.max()),
+        "rel_rmse": float(np.sqrt((err ** 2).sum())) / norm if norm > 0 else float(err.max()),
+        "finite": bool(np.all(np.isfinite(g_gpu))),
+    }
+    rmse_ok = np.sqrt((err ** 2).sum()) <= BWD_REL_RMSE * norm + BWD_ABS_FLOOR * np.sqrt(err.size)
+    ok = stats["finite"] and bool(np.all(err <= allowed)) and bool(rmse_ok)
+    return ok, stats
+
+
+def run_bwd(fa, g, do_bits, causal, scale=None):
+    """The library's forward, then its backward; returns float64
+    ((dq, dk, dv), o) with o the forward output the backward was given."""
+    import torch
+    q, k, v = to_device(g)
+    do = fa_inputs.to_torch_bf16(do_bits, "cuda")
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    grads = tuple(fa_inputs.bf16_bits_to_f64(fa_inputs.bf16_tensor_to_bits(t)) for t in (dq, dk, dv))
+    return grads, fa_inputs.bf16_bits_to_f64(fa_inputs.bf16_tensor_to_bits(o))
+
+
 def to_device(g, device="cuda"):
     q = fa_inputs.to_torch_bf16(g.q_bits, device)
     k = fa_inputs.to_torch_bf16(g.k_bits, device)

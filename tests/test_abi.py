@@ -16,7 +16,7 @@ def declared_functions():
 
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_fp8", "fa_quant_fp8", "fa_status_string", "fa_version"])
+        ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_quant_fp8", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_all_declared(lib):
@@ -89,6 +89,33 @@ def test_fwd_fp8_validation(lib):
     assert call(sv=P + 4) == lib.FA_ERR_MISALIGNED
 
 
+def test_bwd_validation_order(lib):
+    f = lib.lib.fa_bwd
+    args = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=1, N=8, d=128,
+                causal=0, scale=0.1)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                 a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], None)
+
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert call(**{name: None}) == lib.FA_ERR_INVALID_ARG, name
+    assert call(B=0) == lib.FA_ERR_INVALID_ARG
+    assert call(N=0) == lib.FA_ERR_INVALID_ARG
+    assert call(d=256) == lib.FA_ERR_UNSUPPORTED
+    assert call(d=80) == lib.FA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == lib.FA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == lib.FA_ERR_INVALID_ARG
+    assert call(N=1 << 24, d=128) == lib.FA_ERR_TOO_LARGE
+    for name in ("q", "o", "lse", "do", "dv"):
+        assert call(**{name: P + 4}) == lib.FA_ERR_MISALIGNED, name
+    # earlier checks win over later ones
+    assert call(lse=None, d=256) == lib.FA_ERR_INVALID_ARG
+    assert call(d=256, scale=-1.0) == lib.FA_ERR_UNSUPPORTED
+    assert call(scale=-1.0, dq=P + 2) == lib.FA_ERR_INVALID_ARG
+
+
 def test_python_wrapper_rejects_cpu_tensors(lib):
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
@@ -96,3 +123,6 @@ def test_python_wrapper_rejects_cpu_tensors(lib):
         lib.fwd(x, x, x)
     with pytest.raises(TypeError):
         lib.fwd(x.float(), x, x)
+    lse = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError):
+        lib.bwd(x, x, x, x, lse, x)
