@@ -101,6 +101,27 @@ def extras(fa):
                              < RIDGE_BF16 else "mfma"})
         del q, k, v, o, lse
 
+    def run_bwd(name, B, H, N, d, causal, seed, steps=50):
+        q, k, v = device_qkv(B, H, N, d, seed)
+        do_bits, _ = fa_inputs.make_grad(B, H, N, d, seed + fa_inputs.SEEDS["grad_offset"])
+        do = fa_inputs.to_torch_bf16(do_bits, "cuda")
+        o, lse = fa.fwd(q, k, v, causal=causal)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ms = time_calls(lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, dq=dq, dk=dk, dv=dv),
+                        steps, 3)
+        # five N x N x d products (S, dP, dV, dK, dQ) = 2.5 times the forward's two
+        tf = 2.5 * flops(B, H, N, d, causal) / (ms * 1e-3) / 1e12
+        out.append({"name": name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                    "dtype": "bf16", "ms": round(ms, 4), "tflops": round(tf, 1),
+                    "pct_peak": round(100 * tf / PEAK_BF16, 1)})
+        del q, k, v, do, o, lse, dq, dk, dv
+
+    for causal in (False, True):
+        run_bwd("backward (fa_bwd)", 4, 16, 2048, 128, causal, fa_inputs.SEEDS["mid"])
+    for i, d in enumerate((64, 96, 128)):
+        run_bwd("backward head-dim sweep (fa_bwd)", 2, 16, 8192, d, True,
+                fa_inputs.SEEDS["dim_sweep_base"] + i, steps=20)
+
     run("mid causal", 4, 16, 2048, 128, True, fa_inputs.SEEDS["mid"])
     for N in (512, 1024, 2048, 4096, 8192, 16384):
         seed = fa_inputs.SEEDS["seq_sweep_base"] + int(math.log2(N // 512))

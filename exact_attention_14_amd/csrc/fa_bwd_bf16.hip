@@ -37,32 +37,42 @@ namespace {
 
 // --------------------------------------------------------------- pre-pass ---
 
-// Per-row terms of the backward pass, one thread per row r < rows:
+// Per-row terms of the backward pass:
 //   Dout[r]  = sum_c dO[r][c] * O[r][c]   (float32 sums of bf16 products)
 //   NLout[r] = -LSE[r] * log2(e)          (P = exp2(scale log2(e) S + NL))
+// Four lanes per row, each summing D/32 16-byte chunks (chunk c*4 + lane of
+// the row, so that a wave's loads cover 64 contiguous bytes of 16 rows),
+// then a two-step butterfly.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(const u16* __restrict__ O,
                                                        const u16* __restrict__ dO,
                                                        const float* __restrict__ LSE,
                                                        float* __restrict__ Dout,
                                                        float* __restrict__ NLout, long long rows) {
-  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const uint4* o = (const uint4*)(O + r * D);
-  const uint4* g = (const uint4*)(dO + r * D);
+  constexpr int C = D / 32;
+  const long long r = ((long long)blockIdx.x * 256 + threadIdx.x) >> 2;
+  const int j = threadIdx.x & 3;
   float acc = 0.f;
+  if (r < rows) {
+    const uint4* o = (const uint4*)(O + r * D);
+    const uint4* g = (const uint4*)(dO + r * D);
 #pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const uint4 a = o[c], b = g[c];
-    const u16* ea = (const u16*)&a;
-    const u16* eb = (const u16*)&b;
+    for (int c = 0; c < C; ++c) {
+      const uint4 a = o[c * 4 + j], b = g[c * 4 + j];
+      const u16* ea = (const u16*)&a;
+      const u16* eb = (const u16*)&b;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      acc = fmaf(__uint_as_float((unsigned)ea[j] << 16), __uint_as_float((unsigned)eb[j] << 16),
-                 acc);
+      for (int e = 0; e < 8; ++e)
+        acc = fmaf(__uint_as_float((unsigned)ea[e] << 16), __uint_as_float((unsigned)eb[e] << 16),
+                   acc);
+    }
   }
-  Dout[r] = acc;
-  NLout[r] = -LSE[r] * kLog2e;
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  if (r < rows && j == 0) {
+    Dout[r] = acc;
+    NLout[r] = -LSE[r] * kLog2e;
+  }
 }
 
 // 4-byte HBM -> LDS copy per lane (lane l writes lds + 4 l), written as
@@ -83,13 +93,15 @@ __device__ __forceinline__ void copy4_to_lds_asm(i32x4 rsrc, const void* lds, un
 template <int D>
 struct Offsets {
   using G = Geo<D>;
-  int row[G::NK];
-  int tr[G::NO][2];
+  // Chunk 2*kk + half of a row read sits at rb ^ (kk << 5), and the
+  // transposed read of column block i, row group r at t[r] ^ (i << 6): the
+  // swizzle is an XOR on the chunk index, whose bits above the lane's own
+  // come from kk or i.
+  int rb;
+  int t[2];
   __device__ __forceinline__ Offsets(int lane) {
     const int half = lane >> 5, l32 = lane & 31;
-    const int rs = swz<G::CPRP>(l32);
-#pragma unroll
-    for (int kk = 0; kk < G::NK; ++kk) row[kk] = l32 * G::ROWB + (((2 * kk + half) ^ rs) << 4);
+    rb = l32 * G::ROWB + ((half ^ swz<G::CPRP>(l32)) << 4);
     const int g16 = lane >> 4, i16 = lane & 15;
     const int vrow = 4 * half + (i16 >> 2);
     const int vcol = (g16 & 1) * 2 + ((i16 & 3) >> 1);
@@ -97,43 +109,63 @@ struct Offsets {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int rr = vrow + 8 * r;
-      const int sw = swz<G::CPRP>(rr);
-#pragma unroll
-      for (int i = 0; i < G::NO; ++i) tr[i][r] = rr * G::ROWB + (((i * 4 + vcol) ^ sw) << 4) + vbyte;
+      t[r] = rr * G::ROWB + ((vcol ^ swz<G::CPRP>(rr)) << 4) + vbyte;
     }
   }
 };
 
-// A 32 x 32 block of (tile rows of `tile` starting at block row rb*32) x
-// (the 32 lanes' own rows held in `reg`): acc = tile_rows . reg^T.
-template <int D>
-__device__ __forceinline__ f32x16 rows_times_reg(const char* tile, int rb, const Offsets<D>& off,
-                                                 const bf16x8* reg) {
-  f32x16 acc;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < Geo<D>::NK; ++kk) {
-    const bf16x8 a = *(const bf16x8*)(tile + rb * 32 * Geo<D>::ROWB + off.row[kk]);
-    acc = mfma32(a, reg[kk], acc);
-  }
-  return acc;
+// A copy of x that the compiler cannot see through: offsets derived from it
+// are formed next to their use instead of being hoisted out of the loop and
+// held in registers for the whole kernel.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
-// acc[i] += tile^T (d block i x 64 rows) . b, with b[rb][a] the B operand of
-// rows rb*32 + a*16 .. +15 in the permuted order of the transposed reads.
+// acc[i] += (rows rb*32 .. rb*32+31 of `tile`)^T . b, for the d blocks i:
+// b[a] is the B operand of rows rb*32 + a*16 .. +15 in the permuted order of
+// the transposed reads (the order in which a 32x32 product's result rows
+// sit in a lane's registers).
 template <int D>
-__device__ __forceinline__ void tile_t_times(const char* tile, const Offsets<D>& off,
-                                             const bf16x8 (*b)[2], f32x16* acc) {
+__device__ __forceinline__ void block_t_times(const char* tile, int rb, const Offsets<D>& off,
+                                              const bf16x8* b, f32x16* acc) {
+  const int t0 = opaque(off.t[0]), t1 = opaque(off.t[1]);
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int i = 0; i < Geo<D>::NO; ++i) {
+      const char* blk = tile + (rb * 32 + a * 16) * Geo<D>::ROWB;
+      acc[i] = mfma32(tr_pair(blk + (t0 ^ (i << 6)), blk + (t1 ^ (i << 6))), b[a], acc[i]);
+    }
+}
+
+// Two 32x32 products over d that share their A-row offsets:
+// s = (rows rb*32.. of ta) . ra^T and t = (rows rb*32.. of tb) . rb_^T, with
+// each LDS read issued next to the product that consumes it.
+template <int D, bool SCHED = true>
+__device__ __forceinline__ void two_rows_times_reg(const char* ta, const char* tb, int rb,
+                                                   const Offsets<D>& off, const bf16x8* ra,
+                                                   const bf16x8* rbreg, f32x16& s, f32x16& t) {
 #pragma unroll
-      for (int i = 0; i < Geo<D>::NO; ++i) {
-        const char* blk = tile + (rb * 32 + a * 16) * Geo<D>::ROWB;
-        acc[i] = mfma32(tr_pair(blk + off.tr[i][0], blk + off.tr[i][1]), b[rb][a], acc[i]);
-      }
+  for (int v = 0; v < 16; ++v) s[v] = t[v] = 0.f;
+  const int r0 = opaque(off.rb);
+#pragma unroll
+  for (int kk = 0; kk < Geo<D>::NK; ++kk) {
+    const bf16x8 a = *(const bf16x8*)(ta + rb * 32 * Geo<D>::ROWB + (r0 ^ (kk << 5)));
+    s = mfma32(a, ra[kk], s);
+  }
+#pragma unroll
+  for (int kk = 0; kk < Geo<D>::NK; ++kk) {
+    const bf16x8 b = *(const bf16x8*)(tb + rb * 32 * Geo<D>::ROWB + (r0 ^ (kk << 5)));
+    t = mfma32(b, rbreg[kk], t);
+  }
+  if constexpr (SCHED) {
+#pragma unroll
+    for (int kk = 0; kk < Geo<D>::NK; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    }
+  }
 }
 
 // Row fragments of the lane's own row (row < N, else zeros) as B operands.
@@ -150,13 +182,20 @@ __device__ __forceinline__ void load_own_rows(__amdgpu_buffer_rsrc_t r, int row,
 
 // ------------------------------------------------------------------ dK, dV --
 
+// Mask kinds of a step: the steady steps need none. Rows past N need no mask
+// in the dK/dV kernel: their Q and dO rows are copied as zeros and their NL
+// and D as zeros, so P = 1 and dS = 0 there and both products add nothing.
+struct Plain {};
+struct Diagonal {};
+
 // Workgroup: 4 waves x 32 keys = one 128-key tile of one (batch, head); it
 // sweeps the 64-query tiles that attend to it (causal: from its first key
-// on). Q, dO and the query tile's NL and D move HBM -> LDS one tile ahead.
-// Grid: B*H*ceil(N/128); causal key tiles run lowest index (most query
-// tiles) first.
+// on, the first two tiles being the diagonal ones). Q, dO and the query
+// tile's NL and D move HBM -> LDS one tile ahead. Grid: B*H*ceil(N/128);
+// causal key tiles run lowest index (most query tiles) first. Two
+// workgroups share a compute unit (256 registers per lane).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
     u16* __restrict__ dK, u16* __restrict__ dV, int N, int nkt, int nwg, int hpx, float scale) {
@@ -181,7 +220,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const i32x4 rq = make_rsrc_words(Q + head * D, head_bytes);
   const i32x4 rg = make_rsrc_words(dO + head * D, head_bytes);
   // Waves 0 and 1 copy the NL and D rows of a query tile; queries past N
-  // read as zeros (their products are masked).
+  // read as zeros.
   const i32x4 rr = make_rsrc_words((wave == 0 ? NL : Dvec) + head, (unsigned)N * 4u);
 
   const int k0w = kt * 128 + wave * 32;  // first key of the wave
@@ -209,46 +248,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
 
   // Query tile u (in stage st): Q_u in qc, dO_u in gc; tile u+1 goes to the
-  // other stage.
-  auto step = [&](const char* qc, const char* gc, char* qn, char* gn, int st, int u) {
+  // other stage. One 32-query block at a time: S and dP, then P and dS, then
+  // their products, so that only one block's scores are live.
+  auto step = [&](auto kind, const char* qc, const char* gc, char* qn, char* gn, int st, int u) {
+    constexpr bool DIAG = std::is_same_v<decltype(kind), Diagonal>;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (u + 1 < U) issue(qn, gn, st ^ 1, u + 1);
-    const int q0 = u * kBC;
-    bf16x8 pb[2][2], sb[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      // NL and D of the 16 queries this lane holds in block qb: query
-      // qb*32 + 8*g + 4*half + x for element v = 4*g + x.
-      f32x4 nl4[4], d4[4];
+      const int qs = u * kBC + qb * 32;  // first query of the block
+      // Diagonal tiles: a block whose queries all precede the wave's keys
+      // adds nothing (a wave-uniform skip); the block with qs == k0w is
+      // masked element by element (key <= query: l32 <= 8g + 4half + x).
+      if (DIAG && k0w > qs) continue;
+      f32x16 s, dp;
+      two_rows_times_reg<D, false>(qc, gc, qb, off, kreg, vreg, s, dp);  // S = Q K^T, dP = dO V^T
+      bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        nl4[g] = *(const f32x4*)&rowt[st][0][qb * 32 + 8 * g + 4 * half];
-        d4[g] = *(const f32x4*)&rowt[st][1][qb * 32 + 8 * g + 4 * half];
-      }
-      const f32x16 s = rows_times_reg<D>(qc, qb, off, kreg);   // S = Q K^T
-      const f32x16 dp = rows_times_reg<D>(gc, qb, off, vreg);  // dP = dO V^T
-      const bool edge = (q0 + qb * 32 + 32 > N) || (CAUSAL && k0w + 31 > q0 + qb * 32);
+        // NL and D of queries qs + 8g + 4half + x, x = 0..3
+        const f32x4 nl4 = *(const f32x4*)&rowt[st][0][qb * 32 + 8 * g + 4 * half];
+        const f32x4 d4 = *(const f32x4*)&rowt[st][1][qb * 32 + 8 * g + 4 * half];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int q = q0 + qb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-        float p = fast_exp2(fmaf(s[v], c, nl4[v / 4][v % 4]));
-        if (edge && (q >= N || (CAUSAL && kj > q))) p = 0.f;
-        const float ds = p * (dp[v] - d4[v / 4][v % 4]);
-        pb[qb][v / 8][v % 8] = (__bf16)p;
-        sb[qb][v / 8][v % 8] = (__bf16)ds;
+        for (int x = 0; x < 4; ++x) {
+          const int v = 4 * g + x;
+          float p = fast_exp2(fmaf(s[v], c, nl4[x]));
+          if (DIAG && k0w == qs && l32 > 8 * g + 4 * half + x) p = 0.f;
+          pb[v / 8][v % 8] = (__bf16)p;
+          sb[v / 8][v % 8] = (__bf16)(p * (dp[v] - d4[x]));
+        }
       }
+      block_t_times<D>(gc, qb, off, pb, dv);  // dV^T += dO^T P
+      block_t_times<D>(qc, qb, off, sb, dk);  // dK^T += Q^T dS
+      __builtin_amdgcn_sched_barrier(0);
     }
-    tile_t_times<D>(gc, off, pb, dv);  // dV^T += dO^T P
-    tile_t_times<D>(qc, off, sb, dk);  // dK^T += Q^T dS
   };
 
   int u = u0;
-  for (; u + 1 < U; u += 2) {
-    step(qs0, gs0, qs1, gs1, 0, u);
-    step(qs1, gs1, qs0, gs0, 1, u + 1);
+  if constexpr (CAUSAL) {
+    step(Diagonal{}, qs0, gs0, qs1, gs1, 0, u);
+    if (u + 1 < U) step(Diagonal{}, qs1, gs1, qs0, gs0, 1, u + 1);
+    u += 2;
   }
-  if (u < U) step(qs0, gs0, qs1, gs1, 0, u);
+  for (; u + 1 < U; u += 2) {
+    step(Plain{}, qs0, gs0, qs1, gs1, 0, u);
+    step(Plain{}, qs1, gs1, qs0, gs0, 1, u + 1);
+  }
+  if (u < U) step(Plain{}, qs0, gs0, qs1, gs1, 0, u);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();  // every wave is done with the tiles: they hold the staging slots
   static_assert(2 * 32 * 2 * D <= G::TILEB, "two staging slots per tile");
@@ -260,10 +307,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------- dQ --
 
 // Workgroup: 4 waves x 32 queries = one 128-query tile of one (batch, head);
-// it sweeps the 64-key tiles the queries attend to. Grid: B*H*ceil(N/128);
-// causal query tiles run longest first.
+// it sweeps the 64-key tiles the queries attend to. Keys past N are copied
+// as zero rows, but P there is exp(-LSE), not 0, so the tile holding them is
+// masked; so are the two diagonal tiles of a causal sweep (the last two).
+// Grid: B*H*ceil(N/128); causal query tiles run longest first. Two
+// workgroups share a compute unit.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
     u16* __restrict__ dQ, int N, int ntq, int nwg, int hpx, float scale) {
@@ -292,6 +342,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int qi = q0w + l32;
   const int q_last = min(N, qt * 128 + 128) - 1;
   const int T = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
+  // tiles [0, T_plain) need no mask
+  const int T_plain = CAUSAL ? 2 * qt : (N % kBC != 0 ? T - 1 : T);
   const float c = scale * kLog2e;
 
   const CP cp(wave, lane);
@@ -314,37 +366,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int v = 0; v < 16; ++v) dq[i][v] = 0.f;
 
   // Key tile t: K_t in kc, V_t in vc; K_{t+1}, V_{t+1} go to kn, vn.
-  auto step = [&](const char* kc, const char* vc, char* kn, char* vn, int t) {
+  auto step = [&](auto kind, const char* kc, const char* vc, char* kn, char* vn, int t) {
+    constexpr bool MASKED = std::is_same_v<decltype(kind), Diagonal>;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (t + 1 < T) {
       cp.issue(rk, kn, (t + 1) * kBC, wave, true);
       cp.issue(rv, vn, (t + 1) * kBC, wave, true);
     }
-    const int j0 = t * kBC;
-    const bool edge = (j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > q0w);
-    bf16x8 sb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const f32x16 s = rows_times_reg<D>(kc, kb, off, qreg);   // S^T = K Q^T
-      const f32x16 dp = rows_times_reg<D>(vc, kb, off, greg);  // dP^T = V dO^T
+      const int ks = t * kBC + kb * 32;  // first key of the block
+      // a block whose keys all follow the wave's queries adds nothing
+      if (CAUSAL && MASKED && ks > q0w + 31) continue;
+      f32x16 s, dp;
+      two_rows_times_reg<D>(kc, vc, kb, off, qreg, greg, s, dp);  // S^T = K Q^T, dP^T = V dO^T
+      bf16x8 sb[2];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int key = j0 + kb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+        const int key = ks + 8 * (v / 4) + 4 * half + (v % 4);
         float p = fast_exp2(fmaf(s[v], c, nl));
-        if (edge && (key >= N || (CAUSAL && key > qi))) p = 0.f;
-        sb[kb][v / 8][v % 8] = (__bf16)(p * (dp[v] - dd));
+        if (MASKED && (key >= N || (CAUSAL && key > qi))) p = 0.f;
+        sb[v / 8][v % 8] = (__bf16)(p * (dp[v] - dd));
       }
+      __builtin_amdgcn_sched_barrier(0);
+      block_t_times<D>(kc, kb, off, sb, dq);  // dQ^T += K^T dS^T
+#pragma unroll
+      for (int m = 0; m < 2 * G::NO; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    tile_t_times<D>(kc, off, sb, dq);  // dQ^T += K^T dS^T
   };
 
   int t = 0;
-  for (; t + 1 < T; t += 2) {
-    step(ks0, vs0, ks1, vs1, t);
-    step(ks1, vs1, ks0, vs0, t + 1);
+  for (; t + 1 < T_plain; t += 2) {
+    step(Plain{}, ks0, vs0, ks1, vs1, t);
+    step(Plain{}, ks1, vs1, ks0, vs0, t + 1);
   }
-  if (t < T) step(ks0, vs0, ks1, vs1, t);
+  if (t < T_plain) {
+    step(Plain{}, ks0, vs0, ks1, vs1, t);
+    ++t;
+  }
+  // the masked tiles (at most two), stage chosen by parity at run time
+  for (; t < T; ++t) {
+    const bool odd = t & 1;
+    step(Diagonal{}, odd ? ks1 : ks0, odd ? vs1 : vs0, odd ? ks0 : ks1, odd ? vs0 : vs1, t);
+  }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();  // every wave is done with the tiles: they hold the staging slots
   static_assert(2 * 32 * 2 * D <= G::TILEB, "two staging slots per tile");
@@ -359,7 +428,7 @@ hipError_t bwd_launch(const void* q, const void* k, const void* v, const void* o
   const long long rows = (long long)B * H * N;
   float* const dvec = ws;
   float* const nl = ws + rows;
-  hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3((unsigned)((rows * 4 + 255) / 256)), dim3(256), 0,
                      stream, (const u16*)o, (const u16*)dout, lse, dvec, nl, rows);
   const int nt = (N + 127) / 128;
   const long long nwg = (long long)nt * B * H;

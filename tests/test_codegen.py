@@ -1,4 +1,4 @@
-"""Checks on the compiler's gfx950 output for the forward kernels (CPU only:
+"""Checks on the compiler's gfx950 output for the attention kernels (CPU only:
 hipcc cross-compiles to assembly text, nothing runs).
 
 No matrix-core instruction may be issued inside an exec-masked region. The
@@ -17,7 +17,7 @@ import pytest
 
 from exact_attention_14_amd import build as fa_build
 
-KERNELS = ("fa_fwd_bf16.hip", "fa_fp8.hip")
+KERNELS = ("fa_fwd_bf16.hip", "fa_fp8.hip", "fa_bwd_bf16.hip")
 
 
 def _hipcc():
@@ -38,10 +38,10 @@ def device_asm(src, out_dir):
 
 def mfma_under_exec_mask(lines):
     """{kernel: count} of MFMAs between an exec save (s_and_saveexec /
-    s_andn2_saveexec) and the restore of exec, per forward kernel."""
+    s_andn2_saveexec) and the restore of exec, per kernel."""
     bad, kernels, kern, masked = {}, [], None, False
     for line in lines:
-        m = re.match(r"^(_Z\w*fwd_\w*kernel\w*):", line)
+        m = re.match(r"^(_Z\w*(?:fwd|bwd)_\w*kernel\w*):", line)
         if m:
             kern, masked = m.group(1), False
             kernels.append(kern)
