@@ -2,12 +2,13 @@
 """Attention forward throughput on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+                    [--extras-only TEXT]
 
 One step is one fa_fwd call (bf16, non-causal) over the workload
 B=4, H=16, N=2048, d=128 with inputs resident in HBM. The metric is attention
 TFLOP/s = 4*B*H*N^2*d / time (halved for causal masks). Rank 0 prints one JSON
 line. The extra measurements (causal, the sequence and head-dimension sweeps,
-the FP8 path) ride along in "extra"; the CPU baseline times the float64 oracle
+the FP8 path, the backward pass) ride along in "extra"; the CPU baseline times the float64 oracle
 on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -78,12 +79,16 @@ def device_qkv(B, H, N, d, seed, dist="normal"):
     return tuple(fa_inputs.to_torch_bf16(x, "cuda") for x in (g.q_bits, g.k_bits, g.v_bits))
 
 
-def extras(fa):
+def extras(fa, only=None):
+    """The extra measurements; `only` keeps those whose name contains it."""
     import torch
     import fa_inputs
     out = []
+    want = lambda name: only is None or only in name
 
     def run(name, B, H, N, d, causal, seed, dtype=fa.FA_BF16, steps=100):
+        if not want(name):
+            return
         q, k, v = device_qkv(B, H, N, d, seed)
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
@@ -102,6 +107,8 @@ def extras(fa):
         del q, k, v, o, lse
 
     def run_bwd(name, B, H, N, d, causal, seed, steps=50):
+        if not want(name):
+            return
         q, k, v = device_qkv(B, H, N, d, seed)
         do_bits, _ = fa_inputs.make_grad(B, H, N, d, seed + fa_inputs.SEEDS["grad_offset"])
         do = fa_inputs.to_torch_bf16(do_bits, "cuda")
@@ -132,6 +139,8 @@ def extras(fa):
 
     # FP8: B=2 H=16 N=8192 d=128 non-causal, outliers replacing 0.1% of entries,
     # 128-row block scales with the random-sign Hadamard rotation of Q and K.
+    if not want("fp8"):
+        return out
     B, H, N, d = 2, 16, 8192, 128
     g = fa_inputs.make_qkv(B, H, N, d, fa_inputs.SEEDS["fp8"], "outlier_replace")
     q, k, v = (fa_inputs.to_torch_bf16(x, "cuda") for x in (g.q_bits, g.k_bits, g.v_bits))
@@ -209,6 +218,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--extras-only", default=None, metavar="TEXT",
+                    help="run only the extra measurements whose name contains TEXT")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -275,7 +286,7 @@ def main():
     }
     del q, k, v, o, lse
     if not args.no_extras:
-        rec["extra"] = extras(fa)
+        rec["extra"] = extras(fa, args.extras_only)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline()
     print(json.dumps(rec), flush=True)
