@@ -8,8 +8,9 @@ uses it and shares no code, table or helper with it.
 
 Contents
   attention.py  exact softmax(scale * Q K^T) V and per-row log-sum-exp in
-                float64, materialising S and P (pinned: closed forms,
-                brute force, invariants, a library routine).
+                float64, materialising S and P, also for queries and keys of
+                different lengths (pinned: closed forms, brute force,
+                invariants, a library routine).
   attention_grad.py  dQ, dK, dV of sum(dO * O) for the same attention, in
                 float64 (pinned: central finite differences, a library
                 routine's autograd, closed forms, invariants).
@@ -22,6 +23,6 @@ Contents
                 where its inputs are exactly representable (then it equals
                 exact attention up to the rounding of P).
 """
-from .attention import attention, attention_rows, attention_sampled  # noqa: F401
+from .attention import attention, attention_kv, attention_rows, attention_sampled  # noqa: F401
 from .attention_grad import attention_backward  # noqa: F401
 from . import fp8  # noqa: F401

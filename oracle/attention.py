@@ -15,6 +15,12 @@ What is computed follows the plain definition the pages give:
   * the per-row log-sum-exp of the scaled scores, natural logarithm, is
     returned beside O (not on the pages; the reading is LSE_i =
     log sum_j exp(S_ij)).
+  * queries and keys of different lengths (decode: a few new queries against
+    a long key/value cache, which FlashDecoding splits over the key length;
+    droidorbit explainer, FAQ on FlashDecoding): the Nq queries are the last
+    Nq positions of the Nk-long sequence, so with the causal mask query i
+    attends keys j <= i + Nk - Nq (the pages do not say how the positions
+    align; this is the reading for decode, where the new token comes last).
 
 Nothing here is blocked, fused or reordered beyond the definition: each query
 row's scores are formed whole, the row maximum is subtracted for a stable
@@ -75,6 +81,31 @@ def attention(q, k, v, causal=False, scale=None):
             for r0 in range(0, N, ROW_CHUNK):
                 r1 = min(N, r0 + ROW_CHUNK)
                 rows = np.arange(r0, r1)
+                o[b, h, r0:r1], lse[b, h, r0:r1] = attention_rows(
+                    q[b, h, r0:r1], k[b, h], v[b, h], rows, causal, scale)
+    return o, lse
+
+
+def attention_kv(q, k, v, causal=False, scale=None):
+    """Exact attention of [B, H, Nq, d] queries over [B, H, Nk, d] keys and
+    values, the queries placed at positions Nk - Nq .. Nk - 1 (causal needs
+    Nq <= Nk). Returns (o [B, H, Nq, d], lse [B, H, Nq]) in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if causal and Nq > Nk:
+        raise ValueError("causal attention needs Nq <= Nk (every query sees a key)")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty((B, H, Nq, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Nq, ROW_CHUNK):
+                r1 = min(Nq, r0 + ROW_CHUNK)
+                rows = np.arange(r0, r1) + (Nk - Nq)
                 o[b, h, r0:r1], lse[b, h, r0:r1] = attention_rows(
                     q[b, h, r0:r1], k[b, h], v[b, h], rows, causal, scale)
     return o, lse

@@ -219,3 +219,70 @@ def test_input_generator_rounding_and_seeding():
     z = fa_inputs.make_qkv(2, 16, 1024, 128, seed=5, dist="outlier_replace")
     frac = np.mean(np.abs(z.q) > 6)
     assert 2e-4 < frac < 2e-3
+
+
+# --- queries and keys of different lengths (decode) ---------------------------
+
+def brute_force_kv(q, k, v, causal, scale):
+    """Pure-Python loops; query i stands at position i + Nk - Nq."""
+    Nq, Nk, d = len(q), len(k), len(q[0])
+    o = np.zeros((Nq, d))
+    lse = np.zeros(Nq)
+    for i in range(Nq):
+        keys = range(i + Nk - Nq + 1) if causal else range(Nk)
+        s = [scale * math.fsum(q[i][t] * k[j][t] for t in range(d)) for j in keys]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        z = math.fsum(w)
+        for t in range(d):
+            o[i, t] = math.fsum(w[a] * v[j][t] for a, j in enumerate(keys)) / z
+        lse[i] = m + math.log(z)
+    return o, lse
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 1), (1, 7), (3, 9), (5, 5), (4, 11)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_kv_brute_force(Nq, Nk, causal):
+    from oracle import attention_kv
+    d = 5
+    q = _rand((1, 1, Nq, d), 700 + Nq)
+    k, v = _rand((1, 1, Nk, d), 710 + Nk), _rand((1, 1, Nk, d), 720 + Nk)
+    o, lse = attention_kv(q, k, v, causal, 0.7)
+    ob, lb = brute_force_kv(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), causal, 0.7)
+    np.testing.assert_allclose(o[0, 0], ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], lb, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kv_equal_lengths_is_attention(causal):
+    from oracle import attention_kv
+    q, k, v = (_rand((2, 3, 70, 16), 730 + i) for i in range(3))
+    o1, l1 = attention(q, k, v, causal, 0.25)
+    o2, l2 = attention_kv(q, k, v, causal, 0.25)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_kv_identical_keys_mean_over_visible_prefix():
+    """Equal scores: O_i is the mean of V over the keys query i sees, which
+    with the end alignment are keys 0 .. i + Nk - Nq."""
+    from oracle import attention_kv
+    Nq, Nk, d = 6, 40, 8
+    q = _rand((1, 1, Nq, d), 740)
+    k = np.broadcast_to(_rand((d,), 741), (1, 1, Nk, d)).copy()
+    v = _rand((1, 1, Nk, d), 742)
+    o, lse = attention_kv(q, k, v, True, 0.5)
+    for i in range(Nq):
+        n = i + Nk - Nq + 1
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, :n].mean(axis=0), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[0, 0, i], 0.5 * float(q[0, 0, i] @ k[0, 0, 0]) + math.log(n),
+                                   rtol=0, atol=1e-12)
+    o, _ = attention_kv(q, k, v, False, 0.5)
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(v[0, 0].mean(axis=0), (Nq, d)), atol=1e-12)
+
+
+def test_kv_causal_needs_enough_keys():
+    from oracle import attention_kv
+    x = np.zeros((1, 1, 4, 2))
+    with pytest.raises(ValueError):
+        attention_kv(x, x[:, :, :3], x[:, :, :3], True)
