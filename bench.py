@@ -123,6 +123,44 @@ def extras(fa, only=None):
                     "pct_peak": round(100 * tf / PEAK_BF16, 1)})
         del q, k, v, do, o, lse, dq, dk, dv
 
+    def run_split(name, B, H, Nq, Nk, d, causal, seed, steps=100):
+        if not want(name):
+            return
+        gk = fa_inputs.make_qkv(B, H, Nk, d, seed)
+        gq = fa_inputs.make_qkv(B, H, Nq, d, seed + 50000)
+        q = fa_inputs.to_torch_bf16(gq.q_bits, "cuda")
+        k, v = (fa_inputs.to_torch_bf16(x, "cuda") for x in (gk.k_bits, gk.v_bits))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+        ms = time_calls(lambda: fa.fwd_splitkv(q, k, v, causal=causal, out=o, lse=lse), steps, 3)
+        if causal:  # query i sees i + Nk - Nq + 1 keys
+            pairs = Nq * (Nk - Nq) + Nq * (Nq + 1) / 2
+        else:
+            pairs = Nq * Nk
+        fl = 4.0 * B * H * pairs * d
+        nbytes = B * H * (2 * Nk * d * 2 + 2 * Nq * d * 2 + 4 * Nq)
+        rec = {"name": name, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": causal,
+               "dtype": "bf16", "splits": fa.splitkv_splits(B, H, Nq, Nk), "ms": round(ms, 4),
+               "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+               "pct_peak": round(100 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16, 1),
+               "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / PEAK_HBM, 1),
+               "bound": "hbm" if fl / nbytes < RIDGE_BF16 else "mfma"}
+        if Nq == Nk:  # the same problem through fa_fwd, for comparison
+            ms2 = time_calls(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse), steps, 3)
+            rec["fa_fwd_ms"] = round(ms2, 4)
+            rec["fa_fwd_tflops"] = round(fl / (ms2 * 1e-3) / 1e12, 1)
+        out.append(rec)
+        del q, k, v, o, lse
+
+    # decode against a 16k-token cache, one and sixteen new queries per (b, h)
+    for causal in (False, True):
+        run_split("decode split-KV (fa_fwd_splitkv)", 4, 16, 1, 16384, 128, causal, 13000)
+    run_split("decode split-KV (fa_fwd_splitkv)", 1, 16, 16, 65536, 128, True, 13001)
+    # few heads: the key axis fills the compute units that B*H*N/128 cannot
+    run_split("few heads split-KV (fa_fwd_splitkv)", 1, 4, 4096, 4096, 128, True, 13002)
+    run_split("few heads split-KV (fa_fwd_splitkv)", 1, 2, 8192, 8192, 128, False, 13003)
+
     for causal in (False, True):
         run_bwd("backward (fa_bwd)", 4, 16, 2048, 128, causal, fa_inputs.SEEDS["mid"])
     for i, d in enumerate((64, 96, 128)):

@@ -27,7 +27,8 @@ FA_ERR_MISALIGNED = -3
 FA_ERR_HIP = -4
 FA_ERR_TOO_LARGE = -5
 
-EXPORTS = ("fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_bwd", "fa_status_string", "fa_version")
+EXPORTS = ("fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_bwd", "fa_fwd_splitkv", "fa_splitkv_splits",
+           "fa_status_string", "fa_version")
 
 
 class FAError(RuntimeError):
@@ -57,6 +58,10 @@ def _load():
     lib.fa_fwd_fp8.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, fp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_bwd.restype = i
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_splitkv_splits.argtypes = [i, i, i, i, i]
+    lib.fa_splitkv_splits.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -157,6 +162,39 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = 
                         _stream(q8.device))
     _check(st, "fa_fwd_fp8")
     return o, lse
+
+
+def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0,
+                out=None, lse=None, return_lse: bool = True):
+    """Split-KV forward: q bf16 [B, H, Nq, d] against k, v bf16 [B, H, Nk, d];
+    returns (o, lse). Causal places the queries at the last Nq positions."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 [B, H, N, d] tensor")
+        if t.device.type != "cuda" or t.device != q.device:
+            raise ValueError(f"{name} must be on q's GPU")
+    B, H, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError(f"k, v must be [B, H, Nk, d] matching q: {tuple(k.shape)} {tuple(v.shape)}")
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                            int(bool(causal)), float(scale), int(num_splits), _stream(q.device))
+    _check(st, "fa_fwd_splitkv")
+    return o, lse
+
+
+def splitkv_splits(B: int, H: int, Nq: int, Nk: int, num_splits: int = 0) -> int:
+    """The number of key splits fa_fwd_splitkv uses for these sizes."""
+    st = lib.fa_splitkv_splits(B, H, Nq, Nk, num_splits)
+    if st < 0:
+        raise FAError(st, "fa_splitkv_splits")
+    return st
 
 
 def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,

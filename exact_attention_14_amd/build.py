@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa.so")
 OBJ = os.path.join(ROOT, "_build")
 
-SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fp8.hip", "fa_bwd_bf16.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fp8.hip", "fa_bwd_bf16.hip", "fa_fwd_split.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_launch.hpp"
@@ -33,6 +34,49 @@ int sizes_check(int B, int H, int N, int d) {
   return FA_OK;
 }
 
+// Stream-ordered scratch comes from one memory pool per device, created on
+// first use and kept until the process ends. Its release threshold is
+// unlimited, so memory freed at the end of one call is reused by the next
+// call on the stream instead of going back to the driver (with the device's
+// default pool each call paid for a fresh allocation, about 50 us).
+constexpr int kMaxDevices = 64;
+
+hipError_t scratch_pool(hipMemPool_t* out) {
+  static std::mutex mu;
+  static hipMemPool_t pools[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (pools[dev] == nullptr) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      hipMemPoolDestroy(pool);
+      return e;
+    }
+    pools[dev] = pool;
+  }
+  *out = pools[dev];
+  return hipSuccess;
+}
+
+hipError_t scratch_alloc(void** p, size_t bytes, hipStream_t s) {
+  hipMemPool_t pool = nullptr;
+  hipError_t e = scratch_pool(&pool);
+  if (e != hipSuccess) return e;
+  return hipMallocFromPoolAsync(p, bytes, pool, s);
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return FA_OK;
   if (log_enabled()) std::fprintf(stderr, "[fa] %s: %s\n", what, hipGetErrorString(e));
@@ -54,8 +98,8 @@ int run_fp8_path(const void* q, const void* k, const void* v, void* o, float* ls
   const size_t s_bytes = (nblk * sizeof(float) + 255) & ~(size_t)255;
   const size_t total = 3 * t_bytes + 3 * s_bytes + 256 + d * sizeof(float);
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, total, stream);
-  if (e != hipSuccess) return hip_status(e, "hipMallocAsync");
+  hipError_t e = scratch_alloc(&ws, total, stream);
+  if (e != hipSuccess) return hip_status(e, "scratch allocation");
   char* base = static_cast<char*>(ws);
   void* q8 = base;
   void* k8 = base + t_bytes;
@@ -161,13 +205,48 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
                  causal, (double)scale);
   // Stream-ordered scratch: the per-row D and -LSE*log2(e) terms.
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, 2 * (size_t)B * H * N * sizeof(float), s);
-  if (e != hipSuccess) return hip_status(e, "hipMallocAsync");
+  hipError_t e = scratch_alloc(&ws, 2 * (size_t)B * H * N * sizeof(float), s);
+  if (e != hipSuccess) return hip_status(e, "scratch allocation");
   e = fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(ws), B, H, N,
                           d, causal != 0, scale, s);
   hipError_t ef = hipFreeAsync(ws, s);
   if (e != hipSuccess) return hip_status(e, "bwd_bf16 launch");
   return hip_status(ef, "hipFreeAsync");
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int Nq, int Nk, int d, int causal, float scale, int num_splits,
+                   void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && Nq > Nk) return FA_ERR_INVALID_ARG;
+  if (!bwd_dim_ok(d)) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if ((long long)Nk * d > (1LL << 30) || (long long)Nq * d > (1LL << 29) ||
+      (long long)B * H >= (1LL << 31))
+    return FA_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse != nullptr && !aligned16(lse)))
+    return FA_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int splits = fa::split_count(B, H, Nq, Nk, num_splits);
+  if (log_enabled())
+    std::fprintf(stderr, "[fa] fa_fwd_splitkv B=%d H=%d Nq=%d Nk=%d d=%d causal=%d splits=%d\n", B,
+                 H, Nq, Nk, d, causal, splits);
+  // Stream-ordered scratch: the partial outputs and log-sum-exps of the splits.
+  void* ws = nullptr;
+  hipError_t e = scratch_alloc(&ws, (size_t)splits * B * H * Nq * (d + 1) * sizeof(float), s);
+  if (e != hipSuccess) return hip_status(e, "scratch allocation");
+  e = fa::launch_fwd_split_bf16(q, k, v, o, lse, static_cast<float*>(ws), B, H, Nq, Nk, d,
+                                causal != 0, splits, scale, s);
+  hipError_t ef = hipFreeAsync(ws, s);
+  if (e != hipSuccess) return hip_status(e, "fwd_split launch");
+  return hip_status(ef, "hipFreeAsync");
+}
+
+int fa_splitkv_splits(int B, int H, int Nq, int Nk, int num_splits) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0) return FA_ERR_INVALID_ARG;
+  return fa::split_count(B, H, Nq, Nk, num_splits);
 }
 
 const char* fa_status_string(int status) {

@@ -1,0 +1,328 @@
+// Split-KV attention forward (bf16, gfx950): Nq queries of each (batch, head)
+// against Nk keys and values, the key range cut into `splits` parts that
+// run as separate workgroups, their partial results merged by log-sum-exp.
+//
+// This is the FlashDecoding idea (droidorbit FlashAttention-3 explainer, FAQ
+// on FlashDecoding: parallelise over the key/value length, for decode) on
+// the forward's building blocks: when B*H*ceil(Nq/Br) workgroups cannot fill
+// 256 compute units (decode: Nq = 1; or few heads), the key axis supplies the
+// parallelism. With the causal mask the queries are the last Nq positions:
+// query i attends keys j <= i + Nk - Nq.
+//
+// Each workgroup (NW waves, 32 queries per wave, one lane per query as in the
+// forward kernel) runs the online softmax over its split's 64-key tiles and
+// writes, in float32, its partial output normalised by its own row sum and
+// its partial log-sum-exp (-inf when the split holds no key the query
+// attends). A second kernel merges the splits of each row:
+//   LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+#include <math.h>
+
+#include <type_traits>
+
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+#include "fa_tiles_bf16.hpp"
+
+namespace fa {
+namespace {
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_split_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    float* __restrict__ Op, float* __restrict__ Lp, int Nq, int Nk, int nqt, int splits, int tps,
+    int nwg, float scale) {
+  using G = Geo<D>;
+  using CP = TileCopy<D, NW>;
+  constexpr int BR = 32 * NW;  // queries per workgroup
+  __shared__ __attribute__((aligned(1024))) char ks0[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vs0[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char ks1[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vs1[G::TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  // The (query tile, split) items of one head run on one accelerator die
+  // (consecutive logical ids), query tiles fastest: they share the split's
+  // key/value tiles in that die's L2.
+  int bh, rank;
+  tile_of_workgroup(blockIdx.x, nwg, nqt * splits, 0, bh, rank);
+  const int sp = rank / nqt, qt = rank % nqt;
+  const int q0w = qt * BR + wave * 32;
+  const int qi = q0w + l32;
+  const int delta = Nk - Nq;  // causal: query i attends keys <= i + delta
+
+  const int t_all = (Nk + kBC - 1) / kBC;
+  const int t_begin = sp * tps;
+  int t_end = min(t_all, t_begin + tps);
+  if (CAUSAL) t_end = min(t_end, (min(Nq, qt * BR + BR) - 1 + delta) / kBC + 1);
+
+  const size_t qhead = (size_t)bh * (size_t)Nq;
+  const size_t khead = (size_t)bh * (size_t)Nk;
+  const unsigned kv_bytes = (unsigned)Nk * D * 2u;
+  const i32x4 rk = make_rsrc_words(K + khead * D, kv_bytes);
+  const i32x4 rv = make_rsrc_words(V + khead * D, kv_bytes);
+
+  const CP cp(wave, lane);
+  if (t_begin < t_end) {
+    cp.issue(rk, ks0, t_begin * kBC, wave, true);
+    cp.issue(rv, vs0, t_begin * kBC, wave, true);
+  }
+  // Q rows of the lane's query (zeros past Nq) as B operands.
+  bf16x8 qreg[G::NK];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qhead * D, (unsigned)Nq * D * 2u);
+#pragma unroll
+    for (int kk = 0; kk < G::NK; ++kk)
+      qreg[kk] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                      rq, (unsigned)(qi * D + kk * 16 + half * 8) * 2u, 0, 0));
+  }
+
+  // Loop-invariant LDS offsets (the forward kernel's): K rows as A operands,
+  // V read transposed as the A operand of O^T += V^T P^T.
+  int koff[G::NK];
+  {
+    const int kswz = swz<G::CPRP>(l32);
+#pragma unroll
+    for (int kk = 0; kk < G::NK; ++kk) koff[kk] = l32 * G::ROWB + (((2 * kk + half) ^ kswz) << 4);
+  }
+  int voff[G::NO][2];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int vrow = 4 * half + (i16 >> 2);
+    const int vcol = (g16 & 1) * 2 + ((i16 & 3) >> 1);
+    const int vbyte = (i16 & 1) * 8;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = vrow + 8 * r;
+      const int sw = swz<G::CPRP>(row);
+#pragma unroll
+      for (int i = 0; i < G::NO; ++i)
+        voff[i][r] = row * G::ROWB + (((i * 4 + vcol) ^ sw) << 4) + vbyte;
+    }
+  }
+
+  f32x16 oacc[G::NO];
+#pragma unroll
+  for (int i = 0; i < G::NO; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
+  float m_run = -INFINITY;  // running maximum of the raw scores
+  float l_run = 0.f;        // this lane's share of the running row sum
+  const float c = scale * kLog2e;
+
+  auto step = [&](const char* kc, const char* vc, char* kn, char* vn, int t) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (t + 1 < t_end) {
+      cp.issue(rk, kn, (t + 1) * kBC, wave, true);
+      cp.issue(rv, vn, (t + 1) * kBC, wave, true);
+    }
+    const int j0 = t * kBC;
+    // S^T = K Q^T: lane = query, element v of block kb = key
+    // j0 + kb*32 + 8*(v/4) + 4*half + v%4.
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < G::NK; ++kk) {
+        const bf16x8 a = *(const bf16x8*)(kc + kb * 32 * G::ROWB + koff[kk]);
+        s[kb] = mfma32(a, qreg[kk], s[kb]);
+      }
+    }
+    // Keys past Nk (zero rows, score 0) and, causal, keys after the query
+    // position are masked; a wave-uniform test keeps the mask to edge tiles.
+    const bool edge = (j0 + kBC > Nk) || (CAUSAL && j0 + kBC - 1 > q0w + delta);
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = j0 + kb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+        // a select, not a branch: with a lane-dependent branch here the
+        // compiler may move matrix-core products under a partial exec mask
+        const bool drop = edge & ((key >= Nk) | (CAUSAL & (key > qi + delta)));
+        s[kb][v] = drop ? -INFINITY : s[kb][v];
+        mt = fmaxf(mt, s[kb][v]);
+      }
+    const float m_new = fmaxf(m_run, max_with_other_half(mt));
+    // alpha rescales the state to the new maximum; a row that has seen no
+    // key yet keeps -inf and gets P = 0 (no NaN from -inf - -inf).
+    const float alpha = m_new == m_run ? 1.f : fast_exp2((m_run - m_new) * c);
+    const float mb = m_new == -INFINITY ? 0.f : m_new * c;
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < G::NO; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
+    bf16x8 p[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float e = fast_exp2(fmaf(s[kb][v], c, -mb));
+        l_run += e;
+        p[kb][v / 8][v % 8] = (__bf16)e;
+      }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < G::NO; ++i) {
+          const char* blk = vc + (kb * 32 + a * 16) * G::ROWB;
+          oacc[i] = mfma32(tr_pair(blk + voff[i][0], blk + voff[i][1]), p[kb][a], oacc[i]);
+        }
+  };
+
+  int t = t_begin;
+  for (; t + 1 < t_end; t += 2) {
+    step(ks0, vs0, ks1, vs1, t);
+    step(ks1, vs1, ks0, vs0, t + 1);
+  }
+  if (t < t_end) step(ks0, vs0, ks1, vs1, t);
+
+  // Partial results, float32: O_s = O / l (0 where the split holds no key
+  // the query attends) and LSE_s = scale*m + ln l (-inf there). Stores past
+  // Nq fall outside the buffer range and are dropped; no branch.
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse = l_tot > 0.f ? m_run * scale + __logf(l_tot) : -INFINITY;
+  const size_t slab = ((size_t)bh * splits + sp) * (size_t)Nq;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Op + slab * D, (unsigned)Nq * D * 4u);
+#pragma unroll
+  for (int i = 0; i < G::NO; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 w;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) w[x] = oacc[i][4 * g + x] * inv;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, w), ro,
+                                             (unsigned)(qi * D + 32 * i + 8 * g + 4 * half) * 4u,
+                                             0, 0);
+    }
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(Lp + slab, (unsigned)Nq * 4u);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(lse), rl,
+                                        half == 0 ? (unsigned)qi * 4u : kOutOfRange, 0, 0);
+}
+
+// Merge of the splits: one thread per (row, 4 output columns), one pass
+// over the splits with a running maximum (the loads of successive splits
+// do not depend on each other, so several are in flight).
+template <int D>
+__global__ __launch_bounds__(64) void split_combine_kernel(const float* __restrict__ Op,
+                                                           const float* __restrict__ Lp,
+                                                           u16* __restrict__ O,
+                                                           float* __restrict__ LSE, long long rows,
+                                                           int Nq, int splits) {
+  constexpr int C = D / 4;
+  const long long id = (long long)blockIdx.x * 64 + threadIdx.x;
+  if (id >= rows * C) return;
+  const long long r = id / C;
+  const int cc = (int)(id % C);
+  const long long bh = r / Nq;
+  const int i = (int)(r % Nq);
+  const size_t base = (size_t)bh * splits * Nq + i;  // split s at base + s*Nq
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int s = 0; s < splits; ++s) {
+    const float ls = Lp[base + (size_t)s * Nq];
+    const f32x4 o = *(const f32x4*)(Op + (base + (size_t)s * Nq) * D + cc * 4);
+    const float m_new = fmaxf(m, ls);
+    const float f = m == m_new ? 1.f : __expf(m - m_new);  // m = -inf: f = 0
+    const float w = ls == -INFINITY ? 0.f : __expf(ls - m_new);
+    acc = acc * f + w * o;
+    l = l * f + w;
+    m = m_new;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  bf16x4 out;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) out[x] = (__bf16)(acc[x] * inv);
+  *(bf16x4*)(O + r * D + cc * 4) = out;
+  if (LSE != nullptr && cc == 0) LSE[r] = l > 0.f ? m + __logf(l) : -INFINITY;
+}
+
+template <int D, bool CAUSAL, int NW>
+hipError_t split_launch(const void* q, const void* k, const void* v, void* o, float* lse,
+                        float* ws, int B, int H, int Nq, int Nk, int splits, float scale,
+                        hipStream_t stream) {
+  constexpr int BR = 32 * NW;
+  const int nqt = (Nq + BR - 1) / BR;
+  const int t_all = (Nk + kBC - 1) / kBC;
+  const int tps = (t_all + splits - 1) / splits;
+  splits = (t_all + tps - 1) / tps;  // every split non-empty in key range
+  const long long nwg = (long long)B * H * nqt * splits;
+  if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
+  const long long rows = (long long)B * H * Nq;
+  float* const op = ws;
+  float* const lp = ws + rows * splits * D;
+  hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL, NW>), dim3((unsigned)nwg), dim3(64 * NW), 0,
+                     stream, (const u16*)q, (const u16*)k, (const u16*)v, op, lp, Nq, Nk, nqt,
+                     splits, tps, (int)nwg, scale);
+  const long long threads = rows * (D / 4);
+  hipLaunchKernelGGL((split_combine_kernel<D>), dim3((unsigned)((threads + 63) / 64)),
+                     dim3(64), 0, stream, (const float*)op, (const float*)lp, (u16*)o, lse, rows,
+                     Nq, splits);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t split_dispatch(const void* q, const void* k, const void* v, void* o, float* lse,
+                          float* ws, int B, int H, int Nq, int Nk, bool causal, int splits,
+                          float scale, hipStream_t stream) {
+  // One wave per workgroup when the queries fit one wave (decode), else four.
+  if (Nq <= 32)
+    return causal ? split_launch<D, true, 1>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale, stream)
+                  : split_launch<D, false, 1>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale, stream);
+  return causal ? split_launch<D, true, 4>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale, stream)
+                : split_launch<D, false, 4>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale, stream);
+}
+
+}  // namespace
+
+int split_count(int B, int H, int Nq, int Nk, int requested) {
+  const int t_all = (Nk + kBC - 1) / kBC;
+  long long s = requested;
+  if (s <= 0) {
+    const bool decode = Nq <= 32;  // one wave per workgroup
+    const long long base = (long long)B * H * (decode ? 1 : (Nq + 127) / 128);
+    if (decode) {
+      // two rounds of workgroups (two per compute unit), >= 2 key tiles each
+      s = min((1024 + base - 1) / base, (long long)max(1, t_all / 2));
+    } else {
+      // split only below half a round; >= 8 key tiles per split, since every
+      // split adds a float32 partial output to write and merge
+      s = base >= 256 ? 1 : min((512 + base - 1) / base, (long long)max(1, t_all / 8));
+    }
+  }
+  s = max(1LL, min(s, (long long)t_all));
+  const int tps = (int)((t_all + s - 1) / s);
+  return (t_all + tps - 1) / tps;
+}
+
+hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, float* ws, int B, int H, int Nq, int Nk, int d,
+                                 bool causal, int splits, float scale, hipStream_t stream) {
+  switch (d) {
+    case 64:
+      return split_dispatch<64>(q, k, v, o, lse, ws, B, H, Nq, Nk, causal, splits, scale, stream);
+    case 96:
+      return split_dispatch<96>(q, k, v, o, lse, ws, B, H, Nq, Nk, causal, splits, scale, stream);
+    case 128:
+      return split_dispatch<128>(q, k, v, o, lse, ws, B, H, Nq, Nk, causal, splits, scale, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

@@ -27,6 +27,15 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            float* ws, int B, int H, int N, int d, bool causal, float scale,
                            hipStream_t stream);
 
+// Split-KV bf16 forward for Nq queries against Nk keys: d in {64, 96, 128}.
+// ws: split_count(...) * B*H*Nq * (d + 1) floats of scratch.
+hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, float* ws, int B, int H, int Nq, int Nk, int d,
+                                 bool causal, int splits, float scale, hipStream_t stream);
+
+// Number of key splits the split-KV forward uses (requested <= 0: automatic).
+int split_count(int B, int H, int Nq, int Nk, int requested);
+
 // Writes d random signs (+-1) derived from a fixed 64-bit key.
 hipError_t launch_fill_signs(float* signs, int d, unsigned long long key,
                              hipStream_t stream);

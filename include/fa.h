@@ -1,6 +1,7 @@
 /*
  * fa.h - FlashAttention for AMD Instinct MI355X (gfx950), C ABI: the forward
- * pass (bf16 and FP8) and the bf16 backward pass.
+ * pass (bf16 and FP8), a split-KV forward for decode and small batches, and
+ * the bf16 backward pass.
  *
  * The library computes exact scaled-dot-product attention
  *     O = softmax(scale * Q K^T) V,   LSE_i = log sum_j exp(scale * q_i . k_j)
@@ -30,7 +31,12 @@
  *   - Arguments are validated on the host before any HIP call, in the order
  *     listed for each function. No C++ exception crosses this boundary.
  *     Nothing is printed unless the environment variable FA_LOG=1 is set.
- *   - Thread-safe and re-entrant: the library holds no mutable global state.
+ *   - Thread-safe and re-entrant. The only state the library keeps is one
+ *     memory pool per device for stream-ordered scratch (entry points that
+ *     need scratch say so): created on first use under a lock, its memory is
+ *     allocated and freed in stream order (hipMallocFromPoolAsync /
+ *     hipFreeAsync on `stream`) and retained for reuse until the process
+ *     ends, instead of being returned to the driver after every call.
  */
 #ifndef FA_H
 #define FA_H
@@ -68,7 +74,7 @@ typedef enum fa_status {
  *           FA_FP8_E4M3 runs the FP8 path end to end on bf16 inputs: Q and K
  *           are rotated by a fixed random-sign Hadamard matrix and all three
  *           are block-quantised to e4m3 (fa_quant_fp8) into stream-ordered
- *           scratch (hipMallocAsync/hipFreeAsync on `stream`), then
+ *           scratch (the library's pool, on `stream`), then
  *           fa_fwd_fp8 runs. d must be a power of two.
  * Validation order: null q/k/v/o -> INVALID_ARG; B, H or N < 1 -> INVALID_ARG;
  * dtype unknown or d unsupported -> UNSUPPORTED; scale not finite and > 0 ->
@@ -154,8 +160,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
  * d                : 64, 96 or 128
  * Arithmetic: bf16 matrix-core products with float32 accumulation; P and dS
  * are rounded to bf16 as operands of the second products; D is a float32 sum.
- * Scratch: 2 * B*H*N floats, stream-ordered (hipMallocAsync/hipFreeAsync on
- * `stream`).
+ * Scratch: 2 * B*H*N floats, stream-ordered from the library's pool.
  * Validation order: null q/k/v/o/lse/dout/dq/dk/dv -> INVALID_ARG; B, H or
  * N < 1 -> INVALID_ARG; d not in {64, 96, 128} -> UNSUPPORTED; scale not
  * finite and > 0 -> INVALID_ARG; N*d > 2^30 or B*H >= 2^31 -> TOO_LARGE; a
@@ -165,6 +170,42 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_splitkv - attention forward with the key axis split across
+ * workgroups (FlashDecoding: parallelise over the key/value length for
+ * decode; droidorbit FlashAttention-3 explainer, FAQ on FlashDecoding).
+ *
+ * q : bf16 [B, H, Nq, d]       k, v : bf16 [B, H, Nk, d]
+ * o : bf16 [B, H, Nq, d]       lse  : float32 [B, H, Nq] or NULL
+ * d : 64, 96 or 128.   scale : finite > 0.
+ * causal != 0: the queries are the last Nq of the Nk positions, so query i
+ *   attends keys j <= i + Nk - Nq (needs Nq <= Nk). With Nq == Nk this is
+ *   fa_fwd's mask.
+ * num_splits : 0 = automatic: for Nq <= 32 (decode) enough splits for two
+ *   workgroups per compute unit twice over, at least two 64-key tiles each;
+ *   for longer queries a split only when B*H*ceil(Nq/128) < 256, at least
+ *   eight tiles each. Else the number of splits (capped at ceil(Nk/64)).
+ *   The count used is fa_splitkv_splits().
+ * Each split's workgroups write a float32 partial output and log-sum-exp to
+ * stream-ordered scratch from the library's pool (splits * B*H*Nq * (d+1)
+ * floats); a second kernel merges them:
+ *   LSE = log sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s  -> bf16.
+ * The products are the forward's (bf16 operands, fp32 accumulation, P in
+ * bf16); the result differs from fa_fwd's only by rounding order.
+ * Validation order: null q/k/v/o -> INVALID_ARG; B, H, Nq or Nk < 1, or
+ * num_splits < 0 -> INVALID_ARG; causal with Nq > Nk -> INVALID_ARG; d not in
+ * {64, 96, 128} -> UNSUPPORTED; scale not finite and > 0 -> INVALID_ARG;
+ * Nk*d > 2^30, Nq*d > 2^29 or B*H >= 2^31 -> TOO_LARGE; a pointer not 16-byte
+ * aligned -> MISALIGNED; launch or scratch allocation error -> HIP.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                   int num_splits, void* stream);
+
+/* The number of splits fa_fwd_splitkv uses for these sizes (num_splits as
+ * passed to it); INVALID_ARG for sizes < 1 or num_splits < 0. Host only. */
+int fa_splitkv_splits(int B, int H, int Nq, int Nk, int num_splits);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

@@ -16,7 +16,8 @@ def declared_functions():
 
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
-        ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_quant_fp8", "fa_status_string", "fa_version"])
+        ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_quant_fp8", "fa_splitkv_splits",
+         "fa_status_string", "fa_version"])
 
 
 def test_library_exports_all_declared(lib):
@@ -114,6 +115,59 @@ def test_bwd_validation_order(lib):
     assert call(lse=None, d=256) == lib.FA_ERR_INVALID_ARG
     assert call(d=256, scale=-1.0) == lib.FA_ERR_UNSUPPORTED
     assert call(scale=-1.0, dq=P + 2) == lib.FA_ERR_INVALID_ARG
+
+
+def test_splitkv_validation_order(lib):
+    f = lib.lib.fa_fwd_splitkv
+    args = dict(q=P, k=P, v=P, o=P, lse=None, B=1, H=1, Nq=1, Nk=100, d=128, causal=0, scale=0.1,
+                splits=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                 a["causal"], a["scale"], a["splits"], None)
+
+    for name in ("q", "k", "v", "o"):
+        assert call(**{name: None}) == lib.FA_ERR_INVALID_ARG, name
+    assert call(Nq=0) == lib.FA_ERR_INVALID_ARG
+    assert call(Nk=0) == lib.FA_ERR_INVALID_ARG
+    assert call(splits=-1) == lib.FA_ERR_INVALID_ARG
+    assert call(causal=1, Nq=101) == lib.FA_ERR_INVALID_ARG
+    assert call(d=256) == lib.FA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == lib.FA_ERR_INVALID_ARG
+    assert call(Nk=1 << 24) == lib.FA_ERR_TOO_LARGE
+    assert call(Nq=1 << 23, Nk=1 << 23) == lib.FA_ERR_TOO_LARGE
+    assert call(o=P + 8) == lib.FA_ERR_MISALIGNED
+    assert call(lse=P + 4) == lib.FA_ERR_MISALIGNED
+    assert call(q=None, d=256) == lib.FA_ERR_INVALID_ARG
+    assert call(causal=1, Nq=101, d=256) == lib.FA_ERR_INVALID_ARG
+    assert call(d=256, scale=-1.0) == lib.FA_ERR_UNSUPPORTED
+
+
+def test_splitkv_split_count(lib):
+    """Host logic: decode (Nq <= 32) splits into two rounds of workgroups with
+    at least two 64-key tiles each; longer queries split only below half a
+    round, with at least eight tiles per split; never more splits than
+    tiles, and no empty split."""
+    s = lib.splitkv_splits
+    assert s(1, 1, 1, 1) == 1
+    assert s(1, 1, 1, 64 * 10) == 5              # tiles / 2
+    assert s(4, 16, 1, 16384) == 16              # 1024 / 64 workgroups per split
+    assert s(64, 64, 1, 16384) == 1              # enough heads already
+    assert s(1, 1, 1, 64 * 10, 64) == 10         # capped at the tile count
+    assert s(1, 1, 1, 64 * 10, 3) == 3
+    assert s(1, 1, 1, 64 * 10, 4) == 4           # 3 tiles per split, 4 splits
+    assert s(1, 1, 1, 64 * 10, 6) == 5           # 2 tiles per split: 5 non-empty
+    assert s(1, 2, 200, 200, 0) == 1             # 4 tiles: too few to split
+    assert s(1, 4, 4096, 4096) == 4              # 128 workgroups -> 4 splits of 16 tiles
+    assert s(4, 16, 2048, 2048) == 1             # 1024 workgroups: no split
+    with pytest.raises(lib.FAError):
+        s(0, 1, 1, 1)
+    for B, H, Nq, Nk, req in ((1, 1, 1, 777, 0), (2, 3, 40, 5000, 0), (1, 1, 1, 6400, 33)):
+        n = s(B, H, Nq, Nk, req)
+        tiles = -(-Nk // 64)
+        tps = -(-tiles // n)
+        assert 1 <= n <= tiles and (n - 1) * tps < tiles
 
 
 def test_python_wrapper_rejects_cpu_tensors(lib):

@@ -17,7 +17,7 @@ import pytest
 
 from exact_attention_14_amd import build as fa_build
 
-KERNELS = ("fa_fwd_bf16.hip", "fa_fp8.hip", "fa_bwd_bf16.hip")
+KERNELS = ("fa_fwd_bf16.hip", "fa_fp8.hip", "fa_bwd_bf16.hip", "fa_fwd_split.hip")
 
 
 def _hipcc():
