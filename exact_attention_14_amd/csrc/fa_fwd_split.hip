@@ -26,18 +26,25 @@
 namespace fa {
 namespace {
 
-template <int D, bool CAUSAL, int NW>
+// KT keys per tile, S stages in the LDS ring (tiles t+1 .. t+S-2 stay in
+// flight while tile t is used). Decode runs NW = 1, KT = 32, S = 2: 32 KiB of
+// LDS per workgroup (d = 128) lets five workgroups share a compute unit,
+// which streams K and V faster than deeper rings with fewer workgroups
+// (measured: 64 KiB rings of 64-key or 4 x 32-key tiles, two workgroups per
+// unit, reached 10% less). Longer queries run NW = 4, KT = 64, S = 2.
+template <int D, bool CAUSAL, int NW, int KT, int S>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_split_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     float* __restrict__ Op, float* __restrict__ Lp, int Nq, int Nk, int nqt, int splits, int tps,
     int nwg, float scale) {
   using G = Geo<D>;
-  using CP = TileCopy<D, NW>;
-  constexpr int BR = 32 * NW;  // queries per workgroup
-  __shared__ __attribute__((aligned(1024))) char ks0[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char vs0[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char ks1[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char vs1[G::TILEB];
+  using CP = TileCopy<D, NW, KT>;
+  static_assert(KT == 32 || KT == 64, "32- or 64-key tiles");
+  static_assert(S >= 2 && (S - 2) * 2 * CP::NI <= 63, "copies in flight fit the wait counter");
+  constexpr int BR = 32 * NW;   // queries per workgroup
+  constexpr int NB = KT / 32;   // 32-key blocks per tile
+  constexpr int TB = KT * G::ROWB;  // bytes of one K or V tile
+  __shared__ __attribute__((aligned(1024))) char ring[S * 2 * TB];  // stage st: K, then V
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -55,10 +62,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int qi = q0w + l32;
   const int delta = Nk - Nq;  // causal: query i attends keys <= i + delta
 
-  const int t_all = (Nk + kBC - 1) / kBC;
-  const int t_begin = sp * tps;
-  int t_end = min(t_all, t_begin + tps);
-  if (CAUSAL) t_end = min(t_end, (min(Nq, qt * BR + BR) - 1 + delta) / kBC + 1);
+  // tps counts 64-key tiles; this kernel's tiles hold KT keys
+  const int t_all = (Nk + KT - 1) / KT;
+  const int t_begin = sp * tps * (kBC / KT);
+  int t_end = min(t_all, t_begin + tps * (kBC / KT));
+  if (CAUSAL) t_end = min(t_end, (min(Nq, qt * BR + BR) - 1 + delta) / KT + 1);
 
   const size_t qhead = (size_t)bh * (size_t)Nq;
   const size_t khead = (size_t)bh * (size_t)Nk;
@@ -66,11 +74,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const i32x4 rk = make_rsrc_words(K + khead * D, kv_bytes);
   const i32x4 rv = make_rsrc_words(V + khead * D, kv_bytes);
 
-  const CP cp(wave, lane);
-  if (t_begin < t_end) {
-    cp.issue(rk, ks0, t_begin * kBC, wave, true);
-    cp.issue(rv, vs0, t_begin * kBC, wave, true);
-  }
   // Q rows of the lane's query (zeros past Nq) as B operands.
   bf16x8 qreg[G::NK];
   {
@@ -81,6 +84,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                       rq, (unsigned)(qi * D + kk * 16 + half * 8) * 2u, 0, 0));
   }
+  // Let the Q loads land before any tile copy is issued: the compiler does
+  // not see the copies, and a wait for Q placed inside the loop would also
+  // wait for the copies issued ahead there.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  const CP cp(wave, lane);
+  auto issue = [&](int t) {
+    char* const st = ring + ((t - t_begin) % S) * (2 * TB);
+    cp.issue(rk, st, t * KT, wave, true);
+    cp.issue(rv, st + TB, t * KT, wave, true);
+  };
+  for (int t = t_begin; t < min(t_end, t_begin + S - 1); ++t) issue(t);
 
   // Loop-invariant LDS offsets (the forward kernel's): K rows as A operands,
   // V read transposed as the A operand of O^T += V^T P^T.
@@ -115,19 +130,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   float l_run = 0.f;        // this lane's share of the running row sum
   const float c = scale * kLog2e;
 
-  auto step = [&](const char* kc, const char* vc, char* kn, char* vn, int t) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (t + 1 < t_end) {
-      cp.issue(rk, kn, (t + 1) * kBC, wave, true);
-      cp.issue(rv, vn, (t + 1) * kBC, wave, true);
+  for (int t = t_begin; t < t_end; ++t) {
+    // Tile t has landed once at most the copies of tiles t+1 .. t+S-2 are
+    // outstanding (fewer near the end of the split).
+    const int ahead = min(S - 2, t_end - 1 - t);
+    if (ahead <= 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    } else if (ahead == 1) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * CP::NI));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * 2 * CP::NI));
     }
-    const int j0 = t * kBC;
+    __syncthreads();
+    if (t + S - 1 < t_end) issue(t + S - 1);  // into the stage read in step t-1
+    const char* const kc = ring + ((t - t_begin) % S) * (2 * TB);
+    const char* const vc = kc + TB;
+    const int j0 = t * KT;
     // S^T = K Q^T: lane = query, element v of block kb = key
     // j0 + kb*32 + 8*(v/4) + 4*half + v%4.
-    f32x16 s[2];
+    f32x16 s[NB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
 #pragma unroll
@@ -138,10 +161,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     // Keys past Nk (zero rows, score 0) and, causal, keys after the query
     // position are masked; a wave-uniform test keeps the mask to edge tiles.
-    const bool edge = (j0 + kBC > Nk) || (CAUSAL && j0 + kBC - 1 > q0w + delta);
+    const bool edge = (j0 + KT > Nk) || (CAUSAL && j0 + KT - 1 > q0w + delta);
     float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = j0 + kb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
@@ -162,9 +185,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int i = 0; i < G::NO; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
-    bf16x8 p[2][2];
+    bf16x8 p[NB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float e = fast_exp2(fmaf(s[kb][v], c, -mb));
@@ -173,7 +196,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
     // O^T += V^T P^T
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -181,14 +204,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           const char* blk = vc + (kb * 32 + a * 16) * G::ROWB;
           oacc[i] = mfma32(tr_pair(blk + voff[i][0], blk + voff[i][1]), p[kb][a], oacc[i]);
         }
-  };
-
-  int t = t_begin;
-  for (; t + 1 < t_end; t += 2) {
-    step(ks0, vs0, ks1, vs1, t);
-    step(ks1, vs1, ks0, vs0, t + 1);
   }
-  if (t < t_end) step(ks0, vs0, ks1, vs1, t);
 
   // Partial results, float32: O_s = O / l (0 where the split holds no key
   // the query attends) and LSE_s = scale*m + ln l (-inf there). Stores past
@@ -252,7 +268,7 @@ __global__ __launch_bounds__(64) void split_combine_kernel(const float* __restri
   if (LSE != nullptr && cc == 0) LSE[r] = l > 0.f ? m + __logf(l) : -INFINITY;
 }
 
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, int KT, int S>
 hipError_t split_launch(const void* q, const void* k, const void* v, void* o, float* lse,
                         float* ws, int B, int H, int Nq, int Nk, int splits, float scale,
                         hipStream_t stream) {
@@ -266,7 +282,7 @@ hipError_t split_launch(const void* q, const void* k, const void* v, void* o, fl
   const long long rows = (long long)B * H * Nq;
   float* const op = ws;
   float* const lp = ws + rows * splits * D;
-  hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL, NW>), dim3((unsigned)nwg), dim3(64 * NW), 0,
+  hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL, NW, KT, S>), dim3((unsigned)nwg), dim3(64 * NW), 0,
                      stream, (const u16*)q, (const u16*)k, (const u16*)v, op, lp, Nq, Nk, nqt,
                      splits, tps, (int)nwg, scale);
   const long long threads = rows * (D / 4);
@@ -282,10 +298,14 @@ hipError_t split_dispatch(const void* q, const void* k, const void* v, void* o, 
                           float scale, hipStream_t stream) {
   // One wave per workgroup when the queries fit one wave (decode), else four.
   if (Nq <= 32)
-    return causal ? split_launch<D, true, 1>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale, stream)
-                  : split_launch<D, false, 1>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale, stream);
-  return causal ? split_launch<D, true, 4>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale, stream)
-                : split_launch<D, false, 4>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale, stream);
+    return causal ? split_launch<D, true, 1, 32, 2>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale,
+                                                    stream)
+                  : split_launch<D, false, 1, 32, 2>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits,
+                                                     scale, stream);
+  return causal ? split_launch<D, true, 4, 64, 2>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale,
+                                                  stream)
+                : split_launch<D, false, 4, 64, 2>(q, k, v, o, lse, ws, B, H, Nq, Nk, splits, scale,
+                                                   stream);
 }
 
 }  // namespace

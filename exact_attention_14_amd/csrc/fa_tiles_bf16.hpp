@@ -49,11 +49,13 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
 // without memory traffic.
 constexpr unsigned kPadOffset = 0x40000000u;
 
-// Per-lane byte offsets (tile row 0) of this wave's share of a tile copy;
-// rows past the data width get an offset beyond any buffer (zero fill).
-template <int D, int NW>
+// Per-lane byte offsets (tile row 0) of this wave's share of a tile copy of
+// ROWS rows; rows past the data width get an offset beyond any buffer (zero
+// fill).
+template <int D, int NW, int ROWS = kBC>
 struct TileCopy {
-  static constexpr int NI = Geo<D>::CPRP / NW;
+  static constexpr int NI = Geo<D>::CPRP * ROWS / 64 / NW;
+  static_assert(NI * NW * 64 == Geo<D>::CPRP * ROWS, "whole 1 KiB copies per wave");
   unsigned off[NI];
   __device__ __forceinline__ TileCopy(int wave, int lane) {
     using G = Geo<D>;
