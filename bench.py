@@ -163,7 +163,7 @@ def extras(fa, only=None):
 
     for causal in (False, True):
         run_bwd("backward (fa_bwd)", 4, 16, 2048, 128, causal, fa_inputs.SEEDS["mid"])
-    for i, d in enumerate((64, 96, 128)):
+    for i, d in enumerate((64, 96, 128, 256)):
         run_bwd("backward head-dim sweep (fa_bwd)", 2, 16, 8192, d, True,
                 fa_inputs.SEEDS["dim_sweep_base"] + i, steps=20)
 

@@ -24,7 +24,8 @@ bool log_enabled() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool bf16_dim_ok(int d) { return d == 64 || d == 96 || d == 128 || d == 256; }
-bool bwd_dim_ok(int d) { return d == 64 || d == 96 || d == 128; }
+bool bwd_dim_ok(int d) { return d == 64 || d == 96 || d == 128 || d == 256; }
+bool split_dim_ok(int d) { return d == 64 || d == 96 || d == 128; }
 bool fp8_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool pow2(int d) { return d > 0 && (d & (d - 1)) == 0; }
 
@@ -220,7 +221,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && Nq > Nk) return FA_ERR_INVALID_ARG;
-  if (!bwd_dim_ok(d)) return FA_ERR_UNSUPPORTED;
+  if (!split_dim_ok(d)) return FA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if ((long long)Nk * d > (1LL << 30) || (long long)Nq * d > (1LL << 29) ||
       (long long)B * H >= (1LL << 31))

@@ -193,9 +193,10 @@ struct Diagonal {};
 // on, the first two tiles being the diagonal ones). Q, dO and the query
 // tile's NL and D move HBM -> LDS one tile ahead. Grid: B*H*ceil(N/128);
 // causal key tiles run lowest index (most query tiles) first. Two
-// workgroups share a compute unit (256 registers per lane).
+// workgroups share a compute unit (256 registers per lane); at d = 256 the
+// gradients alone take 256 registers and one workgroup runs per unit.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
     u16* __restrict__ dK, u16* __restrict__ dV, int N, int nkt, int nwg, int hpx, float scale) {
@@ -286,16 +287,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   int u = u0;
-  if constexpr (CAUSAL) {
-    step(Diagonal{}, qs0, gs0, qs1, gs1, 0, u);
-    if (u + 1 < U) step(Diagonal{}, qs1, gs1, qs0, gs0, 1, u + 1);
-    u += 2;
+  if constexpr (CAUSAL && D == 256) {
+    // One step kind for the whole sweep: a second copy of the step for the
+    // diagonal tiles pushed this kernel past its 512 registers. Off the
+    // diagonal the kind's tests are wave-uniform and never taken.
+    for (; u + 1 < U; u += 2) {
+      step(Diagonal{}, qs0, gs0, qs1, gs1, 0, u);
+      step(Diagonal{}, qs1, gs1, qs0, gs0, 1, u + 1);
+    }
+    if (u < U) step(Diagonal{}, qs0, gs0, qs1, gs1, 0, u);
+  } else {
+    if constexpr (CAUSAL) {
+      step(Diagonal{}, qs0, gs0, qs1, gs1, 0, u);
+      if (u + 1 < U) step(Diagonal{}, qs1, gs1, qs0, gs0, 1, u + 1);
+      u += 2;
+    }
+    for (; u + 1 < U; u += 2) {
+      step(Plain{}, qs0, gs0, qs1, gs1, 0, u);
+      step(Plain{}, qs1, gs1, qs0, gs0, 1, u + 1);
+    }
+    if (u < U) step(Plain{}, qs0, gs0, qs1, gs1, 0, u);
   }
-  for (; u + 1 < U; u += 2) {
-    step(Plain{}, qs0, gs0, qs1, gs1, 0, u);
-    step(Plain{}, qs1, gs1, qs0, gs0, 1, u + 1);
-  }
-  if (u < U) step(Plain{}, qs0, gs0, qs1, gs1, 0, u);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();  // every wave is done with the tiles: they hold the staging slots
   static_assert(2 * 32 * 2 * D <= G::TILEB, "two staging slots per tile");
@@ -313,7 +325,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // Grid: B*H*ceil(N/128); causal query tiles run longest first. Two
 // workgroups share a compute unit.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
     u16* __restrict__ dQ, int N, int ntq, int nwg, int hpx, float scale) {
@@ -460,6 +472,7 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
     FA_CASE(64)
     FA_CASE(96)
     FA_CASE(128)
+    FA_CASE(256)
     default:
       return hipErrorInvalidValue;
   }

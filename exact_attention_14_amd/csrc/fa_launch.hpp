@@ -21,7 +21,7 @@ hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8,
                           void* o, float* lse, int B, int H, int N, int d,
                           bool causal, float scale, hipStream_t stream);
 
-// bf16 backward: d in {64, 96, 128}. ws: 2*B*H*N floats of scratch.
+// bf16 backward: d in {64, 96, 128, 256}. ws: 2*B*H*N floats of scratch.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            float* ws, int B, int H, int N, int d, bool causal, float scale,

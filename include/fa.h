@@ -157,12 +157,12 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
  *                    returned for the same q, k, v, causal and scale)
  * lse              : float32 [B, H, N] (input, required)
  * dq, dk, dv       : bf16 [B, H, N, d] (outputs; must not alias the inputs)
- * d                : 64, 96 or 128
+ * d                : 64, 96, 128 or 256
  * Arithmetic: bf16 matrix-core products with float32 accumulation; P and dS
  * are rounded to bf16 as operands of the second products; D is a float32 sum.
  * Scratch: 2 * B*H*N floats, stream-ordered from the library's pool.
  * Validation order: null q/k/v/o/lse/dout/dq/dk/dv -> INVALID_ARG; B, H or
- * N < 1 -> INVALID_ARG; d not in {64, 96, 128} -> UNSUPPORTED; scale not
+ * N < 1 -> INVALID_ARG; d not in {64, 96, 128, 256} -> UNSUPPORTED; scale not
  * finite and > 0 -> INVALID_ARG; N*d > 2^30 or B*H >= 2^31 -> TOO_LARGE; a
  * pointer not 16-byte aligned -> MISALIGNED; launch or scratch allocation
  * error -> HIP.

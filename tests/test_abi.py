@@ -104,16 +104,16 @@ def test_bwd_validation_order(lib):
         assert call(**{name: None}) == lib.FA_ERR_INVALID_ARG, name
     assert call(B=0) == lib.FA_ERR_INVALID_ARG
     assert call(N=0) == lib.FA_ERR_INVALID_ARG
-    assert call(d=256) == lib.FA_ERR_UNSUPPORTED
     assert call(d=80) == lib.FA_ERR_UNSUPPORTED
+    assert call(d=512) == lib.FA_ERR_UNSUPPORTED
     assert call(scale=0.0) == lib.FA_ERR_INVALID_ARG
     assert call(scale=float("nan")) == lib.FA_ERR_INVALID_ARG
     assert call(N=1 << 24, d=128) == lib.FA_ERR_TOO_LARGE
     for name in ("q", "o", "lse", "do", "dv"):
         assert call(**{name: P + 4}) == lib.FA_ERR_MISALIGNED, name
     # earlier checks win over later ones
-    assert call(lse=None, d=256) == lib.FA_ERR_INVALID_ARG
-    assert call(d=256, scale=-1.0) == lib.FA_ERR_UNSUPPORTED
+    assert call(lse=None, d=80) == lib.FA_ERR_INVALID_ARG
+    assert call(d=80, scale=-1.0) == lib.FA_ERR_UNSUPPORTED
     assert call(scale=-1.0, dq=P + 2) == lib.FA_ERR_INVALID_ARG
 
 

@@ -54,14 +54,14 @@ def test_small_config(lib, causal):
     check_bwd(lib, 1, 2, 256, 64, causal, fa_inputs.SEEDS["small"])
 
 
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("N", [1, 2, 17, 63, 65, 127, 129, 300])
 def test_ragged_lengths(lib, N, d):
     for causal in (False, True):
         check_bwd(lib, 1, 2, N, d, causal, 9000 + N + d)
 
 
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 def test_several_heads(lib, d):
     # B*H = 24 heads: a multiple of 8 (one run of heads per accelerator die)
     for causal in (False, True):
