@@ -264,6 +264,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
       // masked element by element (key <= query: l32 <= 8g + 4half + x).
       if (DIAG && k0w > qs) continue;
       f32x16 s, dp;
+      // Scores and the P / dS arithmetic at raised issue priority: the other
+      // wave on the SIMD is then usually in its products, and the matrix
+      // core interleaves the two (1-5% measured).
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
       two_rows_times_reg<D, false>(qc, gc, qb, off, kreg, vreg, s, dp);  // S = Q K^T, dP = dO V^T
       bf16x8 pb[2], sb[2];
 #pragma unroll
@@ -280,6 +286,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
           sb[v / 8][v % 8] = (__bf16)(p * (dp[v] - d4[x]));
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
       block_t_times<D>(gc, qb, off, pb, dv);  // dV^T += dO^T P
       block_t_times<D>(qc, qb, off, sb, dk);  // dK^T += Q^T dS
       __builtin_amdgcn_sched_barrier(0);
@@ -392,6 +401,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
       // a block whose keys all follow the wave's queries adds nothing
       if (CAUSAL && MASKED && ks > q0w + 31) continue;
       f32x16 s, dp;
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);  // as in the dK/dV kernel
+      __builtin_amdgcn_sched_barrier(0);
       two_rows_times_reg<D>(kc, vc, kb, off, qreg, greg, s, dp);  // S^T = K Q^T, dP^T = V dO^T
       bf16x8 sb[2];
 #pragma unroll
@@ -401,6 +413,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
         if (MASKED && (key >= N || (CAUSAL && key > qi))) p = 0.f;
         sb[v / 8][v % 8] = (__bf16)(p * (dp[v] - dd));
       }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       block_t_times<D>(kc, kb, off, sb, dq);  // dQ^T += K^T dS^T
 #pragma unroll
