@@ -92,30 +92,29 @@ int check_common(const void* q, const void* k, const void* v, void* o, int B, in
 
 int run_fp8_path(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int H, int N, int d, int causal, float scale, hipStream_t stream) {
-  // Stream-ordered scratch: three e4m3 tensors, three scale arrays, the signs.
+  // Stream-ordered scratch: e4m3 K and V, their block scales, the signs. Q
+  // is quantised inside the forward kernel, block by block, with the same
+  // arithmetic as the quantisation pass.
   const size_t elems = (size_t)B * H * N * d;
   const size_t nblk = (size_t)B * H * ((N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK);
   const size_t t_bytes = (elems + 255) & ~(size_t)255;
   const size_t s_bytes = (nblk * sizeof(float) + 255) & ~(size_t)255;
-  const size_t total = 3 * t_bytes + 3 * s_bytes + 256 + d * sizeof(float);
+  const size_t total = 2 * t_bytes + 2 * s_bytes + 256 + d * sizeof(float);
   void* ws = nullptr;
   hipError_t e = scratch_alloc(&ws, total, stream);
   if (e != hipSuccess) return hip_status(e, "scratch allocation");
   char* base = static_cast<char*>(ws);
-  void* q8 = base;
-  void* k8 = base + t_bytes;
-  void* v8 = base + 2 * t_bytes;
-  float* sq = reinterpret_cast<float*>(base + 3 * t_bytes);
-  float* sk = reinterpret_cast<float*>(base + 3 * t_bytes + s_bytes);
-  float* sv = reinterpret_cast<float*>(base + 3 * t_bytes + 2 * s_bytes);
-  float* signs = reinterpret_cast<float*>(base + 3 * t_bytes + 3 * s_bytes);
+  void* k8 = base;
+  void* v8 = base + t_bytes;
+  float* sk = reinterpret_cast<float*>(base + 2 * t_bytes);
+  float* sv = reinterpret_cast<float*>(base + 2 * t_bytes + s_bytes);
+  float* signs = reinterpret_cast<float*>(base + 2 * t_bytes + 2 * s_bytes);
   e = fa::launch_fill_signs(signs, d, kSignKey, stream);
-  if (e == hipSuccess) e = fa::launch_quant_fp8(q, q8, sq, B, H, N, d, false, signs, stream);
   if (e == hipSuccess) e = fa::launch_quant_fp8(k, k8, sk, B, H, N, d, false, signs, stream);
   if (e == hipSuccess) e = fa::launch_quant_fp8(v, v8, sv, B, H, N, d, false, nullptr, stream);
   if (e == hipSuccess)
-    e = fa::launch_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse, B, H, N, d, causal != 0, scale,
-                           stream);
+    e = fa::launch_fwd_fp8_qbf16(q, signs, k8, v8, sk, sv, o, lse, B, H, N, d, causal != 0, scale,
+                                 stream);
   hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_status(e, "fp8 path launch");
   return hip_status(ef, "hipFreeAsync");

@@ -75,15 +75,99 @@ __device__ __forceinline__ float lane_xor(float v, int m) {
   }
 }
 
+// The arithmetic of one 128-row block, shared by the quantisation pass and
+// the e4m3 forward kernel's quantisation of its own Q block (both therefore
+// give bit-identical codes and scales). 256 threads; thread tid holds chunks
+// cid = k*256 + tid (row cid / CPR, 8 columns from 8 * (cid % CPR)).
+template <int D, bool ROTATE>
+struct BlockQuant {
+  static constexpr int CPR = D / 8;
+  static constexpr int NC = kBlock * CPR / 256;  // chunks per thread
+  static_assert(!ROTATE || (64 % CPR == 0), "rotation needs a row inside one wave");
+  float x[NC][8];
+
+  // Loads the rows from row0 on (zeros past the buffer's end), rotates them
+  // if asked; returns this thread's largest magnitude.
+  __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t rx, int row0,
+                                        const float* __restrict__ signs, int tid) {
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int cid = k * 256 + tid;
+      const int row = cid / CPR, ch = cid % CPR;
+      const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, (unsigned)((row0 + row) * D + ch * 8) * 2u, 0, 0);
+      const u16* e = (const u16*)&w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[k][j] = __uint_as_float((unsigned)e[j] << 16);
+      if constexpr (ROTATE) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[k][j] *= signs[ch * 8 + j];
+        // strides 1, 2, 4 inside the chunk
+#pragma unroll
+        for (int s = 1; s < 8; s <<= 1)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if ((j & s) == 0) {
+              const float a = x[k][j], b = x[k][j + s];
+              x[k][j] = a + b;
+              x[k][j + s] = a - b;
+            }
+        // strides 8 .. D/2 across the lanes holding one row: the lane with
+        // the bit m clear keeps x + other, the one with it set other - x.
+#pragma unroll
+        for (int m = 1; m < CPR; m <<= 1) {
+          const float sgn = (tid & m) ? -1.f : 1.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[k][j] = fmaf(sgn, x[k][j], lane_xor(x[k][j], m));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[k][j]));
+    }
+    return amax;
+  }
+
+  // e4m3 codes of the block, y * inv_s clamped to +-448 and rounded to
+  // nearest even; sink(row, chunk, 8 packed bytes) stores them.
+  template <class Sink>
+  __device__ __forceinline__ void emit(float inv_s, int tid, Sink sink) const {
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int cid = k * 256 + tid;
+      float t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = fminf(fmaxf(x[k][j] * inv_s, -kE4m3Max), kE4m3Max);
+      int lo = cvt_pk_fp8<false>(t[0], t[1], 0);
+      lo = cvt_pk_fp8<true>(t[2], t[3], lo);
+      int hi = cvt_pk_fp8<false>(t[4], t[5], 0);
+      hi = cvt_pk_fp8<true>(t[6], t[7], hi);
+      const i32x2 packed = {lo, hi};
+      sink(cid / CPR, cid % CPR, packed);
+    }
+  }
+};
+
+// Largest of the 256 threads' values (red: 4 floats of LDS; contains a
+// workgroup barrier).
+__device__ __forceinline__ float block_max(float v, float* red, int tid) {
+  v = wave_max(v);
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// The block scale: amax / 448, or 1 for an all-zero block.
+__device__ __forceinline__ float block_scale(float amax) {
+  return amax > 0.f ? amax / kE4m3Max : 1.f;
+}
+
 template <int D, bool ROTATE, int MODE>
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const u16* __restrict__ X,
                                                         uint8_t* __restrict__ X8,
                                                         float* __restrict__ scales,
                                                         const float* __restrict__ signs, int N,
                                                         int nblk, float rsqrt_d) {
-  constexpr int CPR = D / 8;
-  constexpr int NC = kBlock * CPR / 256;  // chunks per thread
-  static_assert(!ROTATE || (64 % CPR == 0), "rotation needs a row inside one wave");
   const int tid = threadIdx.x;
   const int blk = blockIdx.x % nblk;
   const size_t bh = blockIdx.x / nblk;
@@ -93,70 +177,20 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const u16* __restrict__ 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + bh * (size_t)N * D, (unsigned)N * D * 2u);
   const __amdgpu_buffer_rsrc_t rx8 = make_rsrc(X8 + bh * (size_t)N * D, (unsigned)N * D);
 
-  float x[NC][8];
-  float amax = 0.f;
-#pragma unroll
-  for (int k = 0; k < NC; ++k) {
-    const int cid = k * 256 + tid;
-    const int row = cid / CPR, ch = cid % CPR;
-    const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-        rx, (unsigned)((row0 + row) * D + ch * 8) * 2u, 0, 0);
-    const u16* e = (const u16*)&w;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[k][j] = __uint_as_float((unsigned)e[j] << 16);
-    if constexpr (ROTATE) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[k][j] *= signs[ch * 8 + j];
-      // strides 1, 2, 4 inside the chunk
-#pragma unroll
-      for (int s = 1; s < 8; s <<= 1)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if ((j & s) == 0) {
-            const float a = x[k][j], b = x[k][j + s];
-            x[k][j] = a + b;
-            x[k][j + s] = a - b;
-          }
-      // strides 8 .. D/2 across the lanes holding one row: the lane with the
-      // bit m clear keeps x + other, the one with it set other - x.
-#pragma unroll
-      for (int m = 1; m < CPR; m <<= 1) {
-        const float sgn = (tid & m) ? -1.f : 1.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[k][j] = fmaf(sgn, x[k][j], lane_xor(x[k][j], m));
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[k][j]));
-  }
-
+  BlockQuant<D, ROTATE> bq;
   __shared__ float red[4];
-  amax = wave_max(amax);
-  if ((tid & 63) == 0) red[tid >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float amax = block_max(bq.load(rx, row0, signs, tid), red, tid);
   const size_t sidx = bh * nblk + blk;
   if constexpr (MODE == kAmaxOnly) {
     if (tid == 0) scales[sidx] = amax;
     return;
   }
   if constexpr (MODE == kGivenAmax) amax = scales[sidx];
-  const float s = amax > 0.f ? amax / kE4m3Max : 1.f;
+  const float s = block_scale(amax);
   const float inv_s = 1.f / s;  // the scale is applied through its float32 reciprocal
-#pragma unroll
-  for (int k = 0; k < NC; ++k) {
-    const int cid = k * 256 + tid;
-    const int row = cid / CPR, ch = cid % CPR;
-    float t[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = fminf(fmaxf(x[k][j] * inv_s, -kE4m3Max), kE4m3Max);
-    int lo = cvt_pk_fp8<false>(t[0], t[1], 0);
-    lo = cvt_pk_fp8<true>(t[2], t[3], lo);
-    int hi = cvt_pk_fp8<false>(t[4], t[5], 0);
-    hi = cvt_pk_fp8<true>(t[6], t[7], hi);
-    const i32x2 packed = {lo, hi};
+  bq.emit(inv_s, tid, [&](int row, int ch, i32x2 packed) {
     __builtin_amdgcn_raw_buffer_store_b64(packed, rx8, (unsigned)((row0 + row) * D + ch * 8), 0, 0);
-  }
+  });
   if constexpr (MODE == kGivenAmax) __syncthreads();  // every thread has read scales[sidx]
   if (tid == 0) scales[sidx] = ROTATE ? s * rsqrt_d : s;
 }
@@ -276,13 +310,19 @@ struct TileCopy8 {
 //     probabilities the P V product used.
 //   * The reference maximum moves only when a row maximum exceeds it by more
 //     than 0.75 (log2 units), so P * 2^8 <= 2^8.75 = 430 stays within e4m3.
-template <int D, bool CAUSAL, int NW>
+//   * QIN: Q arrives in bf16 and the workgroup quantises its own 128-row Q
+//     block (one quantisation block) in the prologue, with the pass's own
+//     arithmetic (BlockQuant: rotation by the random signs, block amax,
+//     e4m3 codes through LDS into the Q registers): the result is bit for
+//     bit the pre-quantised path's, without Q's round trip through HBM.
+template <int D, bool CAUSAL, int NW, bool QIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
 void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
                     const uint8_t* __restrict__ V8, const float* __restrict__ SQ,
                     const float* __restrict__ SK, const float* __restrict__ SV,
                     u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg,
-                    int hpx, int nblk, float scale) {
+                    int hpx, int nblk, float scale, const u16* __restrict__ Qbf,
+                    const float* __restrict__ signs, float rsqrt_d) {
   using G = Geo8<D>;
   using CP = TileCopy8<D, NW>;
   constexpr int BR = 32 * NW;
@@ -315,20 +355,41 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   const int q_last = min(N, qt * BR + BR) - 1;
   const int T = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
 
-  // Prologue: copy K_0, load Q, copy V_0 and K_1.
+  // Prologue: copy K_0, load (or quantise) Q, copy V_0 and K_1.
   const CP cp(wave, lane);
   cp.issue(rk, ks0, 0, wave, true);
   i32x8 qreg[G::NKS];
+  float sq;
+  if constexpr (QIN) {
+    static_assert(BR == kBlock, "a workgroup's queries are one quantisation block");
+    __shared__ __attribute__((aligned(16))) char qcodes[kBlock * D];
+    __shared__ float red[4];
+    BlockQuant<D, true> bq;
+    const __amdgpu_buffer_rsrc_t rqb = make_rsrc(Qbf + head * D, (unsigned)N * D * 2u);
+    const float s = block_scale(block_max(bq.load(rqb, qt * kBlock, signs, tid), red, tid));
+    bq.emit(1.f / s, tid, [&](int row, int ch, i32x2 packed) {
+      *(i32x2*)(qcodes + row * D + ch * 8) = packed;
+    });
+    __syncthreads();
 #pragma unroll
-  for (int ks = 0; ks < G::NKS; ++ks) {
-    const unsigned off = (unsigned)qi * D + ks * 64 + half * 32;
-    const i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-    const i32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
-    qreg[ks] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int ks = 0; ks < G::NKS; ++ks) {
+      const char* p = qcodes + (wave * 32 + l32) * D + ks * 64 + half * 32;
+      qreg[ks] = __builtin_shufflevector(*(const i32x4*)p, *(const i32x4*)(p + 16), 0, 1, 2, 3,
+                                         4, 5, 6, 7);
+    }
+    sq = s * rsqrt_d;
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < G::NKS; ++ks) {
+      const unsigned off = (unsigned)qi * D + ks * 64 + half * 32;
+      const i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      const i32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
+      qreg[ks] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    sq = sqh[min(qi, N - 1) / kBlock];
   }
   cp.issue(rv, vs0, 0, wave, true);
   cp.issue(rk, ks1, kBC, wave, T > 1);
-  const float sq = sqh[min(qi, N - 1) / kBlock];
 
   f32x16 oacc[G::NO];
 #pragma unroll
@@ -528,10 +589,12 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
                         (m_ref + __log2f(l_tot) - 8.f) * kLn2, slot);
 }
 
+// q8 == nullptr: Q is qbf (bf16), quantised inside the kernel with `signs`.
 template <int D, bool CAUSAL>
 hipError_t fwd_launch(const void* q8, const void* k8, const void* v8, const float* sq,
                       const float* sk, const float* sv, void* o, float* lse, int B, int H, int N,
-                      float scale, hipStream_t stream) {
+                      float scale, hipStream_t stream, const void* qbf = nullptr,
+                      const float* signs = nullptr) {
   constexpr int NW = 4;
   constexpr int BR = 32 * NW;
   const int ntq = (N + BR - 1) / BR;
@@ -539,9 +602,18 @@ hipError_t fwd_launch(const void* q8, const void* k8, const void* v8, const floa
   if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
   const int nblk = (N + kBlock - 1) / kBlock;
   const int hpx = ((long long)B * H) % 8 == 0 ? (int)(((long long)B * H) / 8) : 0;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
-                     stream, (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8, sq, sk,
-                     sv, (u16*)o, lse, N, ntq, (int)nwg, hpx, nblk, scale);
+  if (q8 == nullptr) {
+    const float rsqrt_d = (float)(1.0 / sqrt((double)D));  // as the quantisation pass
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW, true>), dim3((unsigned)nwg), dim3(NW * 64),
+                       0, stream, nullptr, (const uint8_t*)k8, (const uint8_t*)v8, nullptr, sk,
+                       sv, (u16*)o, lse, N, ntq, (int)nwg, hpx, nblk, scale, (const u16*)qbf,
+                       signs, rsqrt_d);
+  } else {
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW, false>), dim3((unsigned)nwg), dim3(NW * 64),
+                       0, stream, (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8, sq,
+                       sk, sv, (u16*)o, lse, N, ntq, (int)nwg, hpx, nblk, scale, nullptr, nullptr,
+                       0.f);
+  }
   return hipGetLastError();
 }
 
@@ -583,6 +655,26 @@ hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const 
                                          stream)                                          \
                   : fwd_launch<DD, false>(q8, k8, v8, sq, sk, sv, o, lse, B, H, N, scale, \
                                           stream);
+  switch (d) {
+    FA_CASE(64)
+    FA_CASE(128)
+    FA_CASE(256)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef FA_CASE
+}
+
+hipError_t launch_fwd_fp8_qbf16(const void* qbf, const float* signs, const void* k8,
+                                const void* v8, const float* sk, const float* sv, void* o,
+                                float* lse, int B, int H, int N, int d, bool causal, float scale,
+                                hipStream_t stream) {
+#define FA_CASE(DD)                                                                           \
+  case DD:                                                                                    \
+    return causal ? fwd_launch<DD, true>(nullptr, k8, v8, nullptr, sk, sv, o, lse, B, H, N,   \
+                                         scale, stream, qbf, signs)                           \
+                  : fwd_launch<DD, false>(nullptr, k8, v8, nullptr, sk, sv, o, lse, B, H, N,  \
+                                          scale, stream, qbf, signs);
   switch (d) {
     FA_CASE(64)
     FA_CASE(128)

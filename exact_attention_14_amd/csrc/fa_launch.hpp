@@ -36,6 +36,13 @@ hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, vo
 // Number of key splits the split-KV forward uses (requested <= 0: automatic).
 int split_count(int B, int H, int Nq, int Nk, int requested);
 
+// FP8 forward with Q in bf16: each workgroup rotates (signs) and quantises
+// its own 128-row Q block exactly as launch_quant_fp8 would.
+hipError_t launch_fwd_fp8_qbf16(const void* qbf, const float* signs, const void* k8,
+                                const void* v8, const float* sk, const float* sv, void* o,
+                                float* lse, int B, int H, int N, int d, bool causal, float scale,
+                                hipStream_t stream);
+
 // Writes d random signs (+-1) derived from a fixed 64-bit key.
 hipError_t launch_fill_signs(float* signs, int d, unsigned long long key,
                              hipStream_t stream);

@@ -186,3 +186,40 @@ def test_fp8_end_to_end_path(lib):
         announce("  causal", causal, "rel_rmse", e,
                  "lse max abs", float(np.abs(lse.cpu().numpy() - lse_ref).max()))
         assert e <= FP8_REL_RMSE
+
+
+def splitmix64_signs(d, key=0x5A17C0DE):
+    """The end-to-end path's fixed signs, from the published SplitMix64
+    definition (Steele, Lea, Flood 2014): sign i is -1 where the top bit of
+    SplitMix64(key + i) is set."""
+    mask = (1 << 64) - 1
+    out = np.empty(d, dtype=np.float32)
+    for i in range(d):
+        x = (key + i + 0x9E3779B97F4A7C15) & mask
+        x = ((x ^ (x >> 30)) * 0xBF58476D1CE4E5B9) & mask
+        x = ((x ^ (x >> 27)) * 0x94D049BB133111EB) & mask
+        x ^= x >> 31
+        out[i] = -1.0 if x >> 63 else 1.0
+    return out
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_end_to_end_equals_explicit_pipeline(lib, d):
+    """fa_fwd(FP8) quantises Q inside the forward kernel; its output must be
+    bit for bit that of fa_quant_fp8 (Q and K rotated by the fixed signs, V
+    plain) followed by fa_fwd_fp8."""
+    import torch
+    for causal in (False, True):
+        B, H, N = 1, 3, 300
+        announce("fp8 end-to-end vs explicit pipeline", B, H, N, d, "causal" if causal else "")
+        g = fa_inputs.make_qkv(B, H, N, d, 730 + d, "outlier_replace")
+        q, k, v = (fa_inputs.to_torch_bf16(b, "cuda") for b in (g.q_bits, g.k_bits, g.v_bits))
+        o1, l1 = lib.fwd(q, k, v, causal=causal, dtype=lib.FA_FP8_E4M3)
+        s = torch.from_numpy(splitmix64_signs(d)).cuda()
+        q8, sq = lib.quant_fp8(q, signs=s)
+        k8, sk = lib.quant_fp8(k, signs=s)
+        v8, sv = lib.quant_fp8(v)
+        o2, l2 = lib.fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1, l2)
