@@ -100,3 +100,26 @@ def test_scale_argument(lib):
         ok, st = bwd_gate(x, r)
         announce("  ", name, st)
         assert ok, (name, st)
+
+
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
+def test_head_dim_sweep_size_sampled_heads(lib, d):
+    """The bench's head-dim sweep workload (B=2 H=16 N=8192 causal) in the
+    launch configuration the bench times; the oracle checks two whole
+    (batch, head) slices, chosen by seed."""
+    import torch
+    B, H, N = 2, 16, 8192
+    seed = fa_inputs.SEEDS["dim_sweep_base"] + (64, 96, 128, 256).index(d)
+    announce("bwd sweep size", B, H, N, d, "causal seed", seed)
+    g = fa_inputs.make_qkv(B, H, N, d, seed)
+    do_bits, do = fa_inputs.make_grad(B, H, N, d, seed + fa_inputs.SEEDS["grad_offset"])
+    got, o = run_bwd(lib, g, do_bits, True)
+    rng = np.random.default_rng(seed)
+    for bh in rng.choice(B * H, size=2, replace=False):
+        b, h = divmod(int(bh), H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = attention_backward(g.q[sl], g.k[sl], g.v[sl], do[sl], True, o=o[sl])
+        for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+            ok, st = bwd_gate(x[sl], r)
+            announce("  ", (b, h), name, st)
+            assert ok, (b, h, name, st)
