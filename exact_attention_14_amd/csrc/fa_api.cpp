@@ -38,7 +38,7 @@ int sizes_check(int B, int H, int N, int d) {
 // Stream-ordered scratch comes from one memory pool per device, created on
 // first use and kept until the process ends. Its release threshold is
 // unlimited, so memory freed at the end of one call is reused by the next
-// call on the stream instead of going back to the driver (with the device's
+// call on the stream instead of being released (with the device's
 // default pool each call paid for a fresh allocation, about 50 us).
 constexpr int kMaxDevices = 64;
 

@@ -36,7 +36,7 @@
  *     need scratch say so): created on first use under a lock, its memory is
  *     allocated and freed in stream order (hipMallocFromPoolAsync /
  *     hipFreeAsync on `stream`) and retained for reuse until the process
- *     ends, instead of being returned to the driver after every call.
+ *     ends, instead of being released after every call.
  */
 #ifndef FA_H
 #define FA_H
