@@ -301,7 +301,7 @@ def main():
     value = f / (ms_per_step * 1e-3) / 1e12
     achieved = f / (kernel_ms * 1e-3) / 1e12
     rec = {
-        "metric": "attention fwd TFLOP/s (4BHN^2d, causal halved) + % of MFMA peak, bf16 & fp8",
+        "metric": "attention fwd TFLOP/s (4BHN\u00b2d, causal halved) + % of MFMA peak, bf16 & fp8",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
