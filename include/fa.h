@@ -24,7 +24,8 @@
  *   - Causal (causal != 0): query i attends key j only when j <= i.
  *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
  *     aligned. The library never frees or keeps them.
- *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream)
+ *     of the calling thread's current device, which also holds the tensors.
  *     Calls only enqueue work and return; the caller keeps buffers alive
  *     until the stream has completed them. Faults inside a kernel surface at
  *     the caller's next synchronisation, not in the return code.
