@@ -123,3 +123,70 @@ def test_head_dim_sweep_size_sampled_heads(lib, d):
             ok, st = bwd_gate(x[sl], r)
             announce("  ", (b, h), name, st)
             assert ok, (b, h, name, st)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_closed_forms_at_mid_size(lib, causal):
+    """Every K row of a head equal: all scores of a query are equal, so
+    P_ij = 1/n_i over the n_i keys it attends (N, or i+1 causal). At the full
+    mid size, without the oracle (D_i = dO_i . O_i with the O the backward is
+    given, as the backward defines it):
+      dV_j = sum_{i attends j} dO_i / n_i,
+      dK_j = scale sum_{i attends j} ((dO_i . V_j) - D_i) Q_i / n_i
+           (non-causal: scale/N (M V_j - sum_i D_i Q_i), M = sum_i Q_i dO_i^T;
+            causal: checked on sampled key rows),
+      dQ_i = scale k sum_j dS_ij = scale k (dO_i . mean_j V_j - D_i) / ... = 0
+           up to D's use of the bf16 O."""
+    import torch
+    B, H, N, d = 4, 16, 2048, 128
+    announce("bwd identical keys", B, H, N, d, "causal" if causal else "noncausal")
+    g = fa_inputs.make_qkv(B, H, N, d, 9700)
+    rng = np.random.default_rng(9701)
+    krow = fa_inputs.bf16_bits(rng.standard_normal((B, H, 1, d), dtype=np.float32))
+    k_bits = np.ascontiguousarray(np.broadcast_to(krow, (B, H, N, d)))
+    do_bits, do = fa_inputs.make_grad(B, H, N, d, 9702)
+    q = fa_inputs.to_torch_bf16(g.q_bits, "cuda")
+    k = fa_inputs.to_torch_bf16(k_bits, "cuda")
+    v = fa_inputs.to_torch_bf16(g.v_bits, "cuda")
+    dot = fa_inputs.to_torch_bf16(do_bits, "cuda")
+    o, lse = lib.fwd(q, k, v, causal=causal)
+    dq, dk, dv = lib.bwd(q, k, v, o, lse, dot, causal=causal)
+    torch.cuda.synchronize()
+    f64 = lambda t: fa_inputs.bf16_bits_to_f64(fa_inputs.bf16_tensor_to_bits(t))
+    dq, dk, dv, o64 = f64(dq), f64(dk), f64(dv), f64(o)
+    qf, vf = g.q, g.v
+    scale = 1.0 / np.sqrt(d)
+    n = np.arange(1, N + 1) if causal else np.full(N, N)
+    D = (do * o64).sum(axis=3)                                   # [B, H, N]
+    w = do / n[None, None, :, None]
+    if causal:
+        dv_ref = np.cumsum(w[:, :, ::-1], axis=2)[:, :, ::-1]
+    else:
+        dv_ref = np.broadcast_to(w.sum(axis=2, keepdims=True), do.shape)
+    ok, st = bwd_gate(dv, dv_ref)
+    announce("   dv", st)
+    assert ok, st
+    if not causal:
+        M = np.einsum("bhic,bhie->bhce", qf, do)                 # sum_i Q_i dO_i^T
+        dk_ref = scale / N * (np.einsum("bhce,bhje->bhjc", M, vf)
+                              - np.einsum("bhi,bhic->bhc", D, qf)[:, :, None, :])
+        ok, st = bwd_gate(dk, dk_ref)
+        announce("   dk", st)
+        assert ok, st
+    else:
+        for (b, h) in ((0, 0), (1, 7), (2, 11), (3, 15)):
+            js = np.array([0, 1, 63, 64, 127, 128, 1000, 2046, 2047] +
+                          list(rng.integers(0, N, 23)))
+            ref = np.empty((len(js), d))
+            for a, j in enumerate(js):
+                i = np.arange(j, N)
+                coef = (do[b, h, i] @ vf[b, h, j] - D[b, h, i]) / n[i]
+                ref[a] = scale * coef @ qf[b, h, i]
+            ok, st = bwd_gate(dk[b, h, js], ref)
+            announce("   dk rows", (b, h), st)
+            assert ok, st
+    # dQ_i = scale k (sum_j P_ij dP_ij - D_i) = scale k dO_i . (O_exact - O)_i
+    bound = scale * np.abs(fa_inputs.bf16_bits_to_f64(krow)).max() * \
+        (np.abs(do) * np.abs(o64)).sum(axis=3).max() * 2.0 ** -8
+    announce("   max|dQ|", float(np.abs(dq).max()), "bound", bound)
+    assert float(np.abs(dq).max()) <= bound + 1e-3
