@@ -29,9 +29,20 @@ bool split_dim_ok(int d) { return d == 64 || d == 96 || d == 128; }
 bool fp8_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool pow2(int d) { return d > 0 && (d & (d - 1)) == 0; }
 
+// A dispatch packet holds the grid size in work-items as a 32-bit number, so
+// every launch (workgroups x threads) must stay at or below 2^32 - 1.
+constexpr long long kMaxWorkItems = 0xFFFFFFFFLL;
+
+// The forward, quantisation and backward kernels run one 256-thread
+// workgroup per 128 rows of a head.
+long long tile_grid_items(int B, int H, int N) {
+  return (long long)((N + 127) / 128) * B * H * 256;
+}
+
 int sizes_check(int B, int H, int N, int d) {
   if ((long long)N * d > (1LL << 30)) return FA_ERR_TOO_LARGE;
   if ((long long)B * H >= (1LL << 31)) return FA_ERR_TOO_LARGE;
+  if (tile_grid_items(B, H, N) > kMaxWorkItems) return FA_ERR_TOO_LARGE;
   return FA_OK;
 }
 
@@ -196,6 +207,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (!(scale > 0.f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   int st = sizes_check(B, H, N, d);
   if (st != FA_OK) return st;
+  // The row-term pass runs four threads per row.
+  if ((long long)B * H * N * 4 > kMaxWorkItems - 255) return FA_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_MISALIGNED;
@@ -225,11 +238,12 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   if ((long long)Nk * d > (1LL << 30) || (long long)Nq * d > (1LL << 29) ||
       (long long)B * H >= (1LL << 31))
     return FA_ERR_TOO_LARGE;
+  const int splits = fa::split_count(B, H, Nq, Nk, num_splits);
+  if (fa::split_work_items(B, H, Nq, d, splits) > kMaxWorkItems) return FA_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse != nullptr && !aligned16(lse)))
     return FA_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int splits = fa::split_count(B, H, Nq, Nk, num_splits);
   if (log_enabled())
     std::fprintf(stderr, "[fa] fa_fwd_splitkv B=%d H=%d Nq=%d Nk=%d d=%d causal=%d splits=%d\n", B,
                  H, Nq, Nk, d, causal, splits);

@@ -15,6 +15,7 @@
 // its partial log-sum-exp (-inf when the split holds no key the query
 // attends). A second kernel merges the splits of each row:
 //   LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+#include <algorithm>
 #include <math.h>
 
 #include <type_traits>
@@ -329,16 +330,25 @@ int split_count(int B, int H, int Nq, int Nk, int requested) {
     const long long base = (long long)B * H * (decode ? 1 : (Nq + 127) / 128);
     if (decode) {
       // two rounds of workgroups (two per compute unit), >= 2 key tiles each
-      s = min((1024 + base - 1) / base, (long long)max(1, t_all / 2));
+      s = std::min<long long>((1024 + base - 1) / base, std::max(1, t_all / 2));
     } else {
       // split only below half a round; >= 8 key tiles per split, since every
       // split adds a float32 partial output to write and merge
-      s = base >= 256 ? 1 : min((512 + base - 1) / base, (long long)max(1, t_all / 8));
+      s = base >= 256 ? 1 : std::min<long long>((512 + base - 1) / base, std::max(1, t_all / 8));
     }
   }
-  s = max(1LL, min(s, (long long)t_all));
+  s = std::max<long long>(1, std::min<long long>(s, t_all));
   const int tps = (int)((t_all + s - 1) / s);
   return (t_all + tps - 1) / tps;
+}
+
+long long split_work_items(int B, int H, int Nq, int d, int splits) {
+  // Split kernel: one wave per 32 queries (Nq <= 32) or four per 128; the
+  // merge: d/4 threads per query row in 64-thread workgroups.
+  const int nw = Nq <= 32 ? 1 : 4;
+  const long long split_items = (long long)B * H * ((Nq + 32 * nw - 1) / (32 * nw)) * splits * 64 * nw;
+  const long long merge_items = ((long long)B * H * Nq * (d / 4) + 63) / 64 * 64;
+  return split_items > merge_items ? split_items : merge_items;
 }
 
 hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, void* o,

@@ -36,6 +36,10 @@ hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, vo
 // Number of key splits the split-KV forward uses (requested <= 0: automatic).
 int split_count(int B, int H, int Nq, int Nk, int requested);
 
+// Work-items (workgroups x threads) of the larger of the split-KV forward's
+// two launches, for the grid-size check.
+long long split_work_items(int B, int H, int Nq, int d, int splits);
+
 // FP8 forward with Q in bf16: each workgroup rotates (signs) and quantises
 // its own 128-row Q block exactly as launch_quant_fp8 would.
 hipError_t launch_fwd_fp8_qbf16(const void* qbf, const float* signs, const void* k8,

@@ -57,7 +57,8 @@ typedef enum fa_status {
     FA_ERR_UNSUPPORTED = -2,   /* head dimension or dtype not instantiated       */
     FA_ERR_MISALIGNED = -3,    /* a tensor pointer is not 16-byte aligned        */
     FA_ERR_HIP = -4,           /* the HIP runtime reported an error at launch    */
-    FA_ERR_TOO_LARGE = -5      /* N*d above 2^30 or B*H above the 32-bit range  */
+    FA_ERR_TOO_LARGE = -5      /* N*d above 2^30, B*H above the 32-bit range, or
+                                  a launch grid above 2^32 - 1 work-items     */
 } fa_status;
 
 /* Rows per FP8 quantisation block: one fp32 scale per 128 consecutive
@@ -85,8 +86,10 @@ typedef enum fa_status {
  *           before mixing). d must be a power of two.
  * Validation order: null q/k/v/o -> INVALID_ARG; B, H or N < 1 -> INVALID_ARG;
  * dtype unknown or d unsupported -> UNSUPPORTED; scale not finite and > 0 ->
- * INVALID_ARG; N*d > 2^30 or B*H >= 2^31 -> TOO_LARGE; a pointer not 16-byte
- * aligned -> MISALIGNED; launch (or scratch allocation) error -> HIP.
+ * INVALID_ARG; N*d > 2^30, B*H >= 2^31 or B*H*ceil(N/128) >= 2^24 (one
+ * 256-thread workgroup per 128 rows; a dispatch counts at most 2^32 - 1
+ * work-items) -> TOO_LARGE; a pointer not 16-byte aligned -> MISALIGNED;
+ * launch (or scratch allocation) error -> HIP.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, int causal, float scale, int dtype,
@@ -170,7 +173,9 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
  * Scratch: 2 * B*H*N floats, stream-ordered from the library's pool.
  * Validation order: null q/k/v/o/lse/dout/dq/dk/dv -> INVALID_ARG; B, H or
  * N < 1 -> INVALID_ARG; d not in {64, 96, 128, 256} -> UNSUPPORTED; scale not
- * finite and > 0 -> INVALID_ARG; N*d > 2^30 or B*H >= 2^31 -> TOO_LARGE; a
+ * finite and > 0 -> INVALID_ARG; N*d > 2^30, B*H >= 2^31,
+ * B*H*ceil(N/128) >= 2^24 or B*H*N >= 2^30 (the grid limit of 2^32 - 1
+ * work-items; four threads per row in the row-term pass) -> TOO_LARGE; a
  * pointer not 16-byte aligned -> MISALIGNED; launch or scratch allocation
  * error -> HIP.
  */
@@ -203,8 +208,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * Validation order: null q/k/v/o -> INVALID_ARG; B, H, Nq or Nk < 1, or
  * num_splits < 0 -> INVALID_ARG; causal with Nq > Nk -> INVALID_ARG; d not in
  * {64, 96, 128} -> UNSUPPORTED; scale not finite and > 0 -> INVALID_ARG;
- * Nk*d > 2^30, Nq*d > 2^29 or B*H >= 2^31 -> TOO_LARGE; a pointer not 16-byte
- * aligned -> MISALIGNED; launch or scratch allocation error -> HIP.
+ * Nk*d > 2^30, Nq*d > 2^29, B*H >= 2^31, or either launch above 2^32 - 1
+ * work-items (split kernel: 64 threads per 32 queries per split; merge: d/4
+ * threads per query row) -> TOO_LARGE; a pointer not 16-byte aligned ->
+ * MISALIGNED; launch or scratch allocation error -> HIP.
  */
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int Nq, int Nk, int d, int causal, float scale,

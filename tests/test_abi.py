@@ -54,6 +54,12 @@ def test_fwd_validation_order(lib):
     assert fwd(lib, scale=float("nan")) == lib.FA_ERR_INVALID_ARG
     assert fwd(lib, scale=float("inf")) == lib.FA_ERR_INVALID_ARG
     assert fwd(lib, N=1 << 25, d=64) == lib.FA_ERR_TOO_LARGE
+    # a launch of 2^24 workgroups of 256 threads exceeds the 32-bit grid size
+    assert fwd(lib, B=1 << 12, H=1 << 12, N=1) == lib.FA_ERR_TOO_LARGE
+    assert fwd(lib, B=1 << 12, H=1 << 12, N=1, dtype=lib.FA_FP8_E4M3) == lib.FA_ERR_TOO_LARGE
+    assert fwd(lib, B=1 << 11, H=1 << 12, N=129) == lib.FA_ERR_TOO_LARGE
+    # just below the limit the size check passes and the next check decides
+    assert fwd(lib, B=1 << 12, H=(1 << 12) - 1, N=128, q=P + 2) == lib.FA_ERR_MISALIGNED
     assert fwd(lib, q=P + 2) == lib.FA_ERR_MISALIGNED
     assert fwd(lib, lse=P + 4) == lib.FA_ERR_MISALIGNED
     # earlier checks win over later ones
@@ -70,6 +76,7 @@ def test_quant_validation(lib):
     assert q(P, P, P, 1, 1, 8, 72, 0, None, None) == lib.FA_ERR_UNSUPPORTED
     assert q(P, P, P, 1, 1, 8, 96, 0, P, None) == lib.FA_ERR_UNSUPPORTED   # rotation needs 2^k
     assert q(P, P + 8, P, 1, 1, 8, 64, 0, None, None) == lib.FA_ERR_MISALIGNED
+    assert q(P, P, P, 1 << 12, 1 << 12, 8, 64, 0, None, None) == lib.FA_ERR_TOO_LARGE
 
 
 def test_fwd_fp8_validation(lib):
@@ -88,6 +95,7 @@ def test_fwd_fp8_validation(lib):
     assert call(d=96) == lib.FA_ERR_UNSUPPORTED
     assert call(scale=0.0) == lib.FA_ERR_INVALID_ARG
     assert call(sv=P + 4) == lib.FA_ERR_MISALIGNED
+    assert call(B=1 << 12, H=1 << 12) == lib.FA_ERR_TOO_LARGE
 
 
 def test_bwd_validation_order(lib):
@@ -109,6 +117,10 @@ def test_bwd_validation_order(lib):
     assert call(scale=0.0) == lib.FA_ERR_INVALID_ARG
     assert call(scale=float("nan")) == lib.FA_ERR_INVALID_ARG
     assert call(N=1 << 24, d=128) == lib.FA_ERR_TOO_LARGE
+    assert call(B=1 << 12, H=1 << 12, N=1) == lib.FA_ERR_TOO_LARGE
+    # 2^30 rows: the row-term pass would need 2^32 threads (the tile grid fits)
+    assert call(B=1 << 10, H=1 << 10, N=1 << 10, d=64) == lib.FA_ERR_TOO_LARGE
+    assert call(B=1 << 10, H=(1 << 10) - 1, N=1 << 10, d=64, dq=P + 2) == lib.FA_ERR_MISALIGNED
     for name in ("q", "o", "lse", "do", "dv"):
         assert call(**{name: P + 4}) == lib.FA_ERR_MISALIGNED, name
     # earlier checks win over later ones
@@ -137,6 +149,10 @@ def test_splitkv_validation_order(lib):
     assert call(scale=0.0) == lib.FA_ERR_INVALID_ARG
     assert call(Nk=1 << 24) == lib.FA_ERR_TOO_LARGE
     assert call(Nq=1 << 23, Nk=1 << 23) == lib.FA_ERR_TOO_LARGE
+    # decode, one split: 2^26 one-wave workgroups = 2^32 work-items
+    assert call(B=1 << 13, H=1 << 13, Nk=64) == lib.FA_ERR_TOO_LARGE
+    # just below the limit the size check passes and the next check decides
+    assert call(B=1 << 13, H=(1 << 13) - 1, Nk=64, o=P + 8) == lib.FA_ERR_MISALIGNED
     assert call(o=P + 8) == lib.FA_ERR_MISALIGNED
     assert call(lse=P + 4) == lib.FA_ERR_MISALIGNED
     assert call(q=None, d=256) == lib.FA_ERR_INVALID_ARG
