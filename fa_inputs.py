@@ -20,6 +20,10 @@ Workloads (all synthetic; the pages measure on synthetic data themselves):
   * an upstream gradient dO for the backward pass: iid N(0,1) entries of the
     output's shape, rounded to bf16 (the pages give no distribution for it;
     this is the plainest choice, the same as the inputs').
+  * for tensors of more than 2^31 elements (the size-limit tests), iid N(0,1)
+    entries drawn on the device by torch's seeded generator and rounded to
+    bf16 there; the oracle receives the bf16 patterns of the heads it checks,
+    copied back, so both sides still see the same values.
 """
 from __future__ import annotations
 
@@ -112,6 +116,21 @@ def bf16_tensor_to_bits(t) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
+def device_normal_bf16(shape, seed, device="cuda", chunk=1 << 27):
+    """A torch.bfloat16 tensor of iid N(0,1) entries drawn on `device` by
+    torch's generator seeded with `seed`, in float32 chunks of `chunk`
+    elements rounded to bf16 on the device."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    for s in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - s)
+        flat[s:s + n] = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+    return out
+
+
 # Seeds are fixed per workload in advance.
 SEEDS = {
     "small": 1,          # B=1 H=2 N=256 d=64
@@ -121,4 +140,5 @@ SEEDS = {
     "fp8": 5,
     "fp8_signs": 55,
     "grad_offset": 100000,   # dO seed = the Q/K/V seed + this offset
+    "large": 600,        # tensors of more than 2^31 elements (device-drawn)
 }
