@@ -142,14 +142,16 @@ def test_fwd_fp8_causal_row0_closed_form(lib):
     np.testing.assert_allclose(o_gpu[:, :, 0], expect, rtol=2 ** -8, atol=0)
 
 
-def test_fp8_config_full_size_sampled(lib):
-    """B=2 H=16 N=8192 d=128, outliers replacing 0.1% of entries, block
-    scales with Hadamard rotation; beside it the variants without rotation and
-    with one scale per tensor."""
+@pytest.mark.parametrize("dist", ["outlier_replace", "outlier_add"])
+def test_fp8_config_full_size_sampled(lib, dist):
+    """B=2 H=16 N=8192 d=128, outliers replacing 0.1% of entries (and the
+    QbitAI article's additive wording of the same model), block scales with
+    Hadamard rotation; beside it the variants without rotation and with one
+    scale per tensor."""
     import torch
-    announce("fp8 full config sampled")
+    announce("fp8 full config sampled", dist)
     B, H, N, d = 2, 16, 8192, 128
-    g = fa_inputs.make_qkv(B, H, N, d, fa_inputs.SEEDS["fp8"], "outlier_replace")
+    g = fa_inputs.make_qkv(B, H, N, d, fa_inputs.SEEDS["fp8"], dist)
     signs = fa_inputs.random_signs(d, fa_inputs.SEEDS["fp8_signs"])
     rows = sample_rows(B, H, N, 128, 11)
     o_ref, _ = attention_sampled(g.q, g.k, g.v, rows, False)
