@@ -196,7 +196,7 @@ struct Diagonal {};
 // workgroups share a compute unit (256 registers per lane); at d = 256 the
 // gradients alone take 256 registers and one workgroup runs per unit.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
     u16* __restrict__ dK, u16* __restrict__ dV, int N, int nkt, int nwg, int hpx, float scale) {
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
 // Grid: B*H*ceil(N/128); causal query tiles run longest first. Two
 // workgroups share a compute unit.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void bwd_dq_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
     u16* __restrict__ dQ, int N, int ntq, int nwg, int hpx, float scale) {

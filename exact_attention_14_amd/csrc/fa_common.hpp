@@ -54,6 +54,16 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // traffic.
 constexpr unsigned kOutOfRange = 0x80000000u;
 
+// Waves per SIMD the attention kernels are compiled for (their register
+// budget: 512 / waves per lane). d = 256 needs the whole file for one wave;
+// d = 64 fits three (<= 168 registers): measured on the forward +2% (bf16)
+// and +5 to +9% (e4m3) at N = 8192, +5 to +13% (bf16) at N = 1024, -3% at
+// N = 2048 non-causal (1024 workgroups: 1.33 rounds of three per compute
+// unit instead of two rounds of two), and on the backward +2 to +5% at
+// N = 8192; the rest run two.
+template <int D>
+constexpr int kWavesPerSimd = D == 256 ? 1 : (D == 64 ? 3 : 2);
+
 // Instruction classes of __builtin_amdgcn_sched_group_barrier masks.
 constexpr int kSchedValu = 0x002 | 0x400;  // VALU and transcendental
 constexpr int kSchedMfma = 0x008;

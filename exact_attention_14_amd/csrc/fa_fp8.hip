@@ -316,7 +316,7 @@ struct TileCopy8 {
 //     e4m3 codes through LDS into the Q registers): the result is bit for
 //     bit the pre-quantised path's, without Q's round trip through HBM.
 template <int D, bool CAUSAL, int NW, bool QIN>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>)))
 void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
                     const uint8_t* __restrict__ V8, const float* __restrict__ SQ,
                     const float* __restrict__ SK, const float* __restrict__ SV,

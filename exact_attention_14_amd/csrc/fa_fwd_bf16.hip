@@ -52,7 +52,7 @@ constexpr float kLazyLog2 = 8.f; // rescale threshold, log2 units
 // one tile further ahead than V through two-stage LDS rings; the copies are
 // issued as assembly so that only the kernel's own waits order them.
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2))) void fwd_bf16_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg, int hpx, float scale) {
   using G = Geo<D>;

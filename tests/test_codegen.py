@@ -75,3 +75,49 @@ def test_no_mfma_under_partial_exec(src, tmp_path):
     kernels, bad = mfma_under_exec_mask(device_asm(src, str(tmp_path)))
     assert len(kernels) >= 6, kernels
     assert bad == {}, f"MFMAs inside exec-masked regions: {bad}"
+
+
+def kernel_resources(lines):
+    """{kernel: (registers incl. accumulation registers, scratch bytes)} from
+    the code-object descriptors in the assembly."""
+    out, name, regs, scratch = {}, None, None, None
+    for line in lines:
+        s = line.strip()
+        if s.startswith(".amdhsa_kernel "):
+            name, regs, scratch = s.split()[1], None, None
+        elif name and s.startswith(".amdhsa_next_free_vgpr "):
+            regs = int(s.split()[1])
+        elif name and s.startswith(".amdhsa_private_segment_fixed_size "):
+            scratch = int(s.split()[1])
+        elif name and s.startswith(".end_amdhsa_kernel"):
+            out[name] = (regs, scratch)
+            name = None
+    return out
+
+
+def intended_waves(name):
+    """Waves per SIMD the attention kernels are compiled for: one at d = 256,
+    three at d = 64 (not the split-KV kernel), two otherwise."""
+    d = int(re.search(r"kernelILi(\d+)E", name).group(1))
+    if d == 256:
+        return 1
+    if d == 64 and "fwd_split_kernel" not in name:
+        return 3
+    return 2
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+@pytest.mark.parametrize("src", KERNELS)
+def test_register_budget_and_no_spills(src, tmp_path):
+    """Every attention kernel fits the register budget of its occupancy (512
+    registers per lane shared by the waves of a SIMD, allocated in blocks of
+    8) and spills nothing to scratch."""
+    res = kernel_resources(device_asm(src, str(tmp_path)))
+    main = {k: v for k, v in res.items()
+            if re.search(r"(fwd_bf16|fwd_fp8|bwd_dkdv|bwd_dq|fwd_split)_kernel", k)}
+    assert len(main) >= 6, sorted(res)
+    for name, (regs, scratch) in main.items():
+        waves = intended_waves(name)
+        budget = (512 // waves) // 8 * 8
+        assert scratch == 0, (name, scratch)
+        assert (regs + 7) // 8 * 8 <= budget, (name, regs, waves)
