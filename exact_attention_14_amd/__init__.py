@@ -94,6 +94,18 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _check_buf(t, name, shape, dtype, device):
+    """A caller-provided output or side input must match exactly what the
+    kernels read or write: contiguous, this dtype, shape and device."""
+    if t is None:
+        return
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
 def _check_qkv(q, k, v, dtype):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -121,6 +133,8 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, dtype: int = 
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _check_buf(out, "out", q.shape, torch.bfloat16, q.device)
+    _check_buf(lse, "lse", (B, H, N), torch.float32, q.device)
     o = torch.empty_like(q) if out is None else out
     if lse is None and return_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -135,12 +149,15 @@ def quant_fp8(x, per_tensor: bool = False, signs=None, out=None, scales=None):
     import torch
     if x.dtype != torch.bfloat16 or x.dim() != 4 or not x.is_contiguous():
         raise ValueError("x must be a contiguous bf16 [B, H, N, d] tensor")
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a GPU")
     B, H, N, d = x.shape
     nblk = (N + FP8_BLOCK - 1) // FP8_BLOCK
+    _check_buf(out, "out", x.shape, torch.float8_e4m3fn, x.device)
+    _check_buf(scales, "scales", (B, H, nblk), torch.float32, x.device)
+    _check_buf(signs, "signs", (d,), torch.float32, x.device)
     x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device) if out is None else out
     sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device) if scales is None else scales
-    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d):
-        raise ValueError("signs must be a float32 tensor of d entries")
     st = lib.fa_quant_fp8(_ptr(x), _ptr(x8), _ptr(sc), B, H, N, d, int(bool(per_tensor)),
                           _ptr(signs), _stream(x.device))
     _check(st, "fa_quant_fp8")
@@ -152,6 +169,13 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = 
     """Attention forward on e4m3fn operands with block scales; returns (o bf16, lse)."""
     torch = _check_qkv(q8, k8, v8, _fp8())
     B, H, N, d = q8.shape
+    nblk = (N + FP8_BLOCK - 1) // FP8_BLOCK
+    for name, t in (("sq", sq), ("sk", sk), ("sv", sv)):
+        if t is None:
+            raise ValueError(f"{name} is required")
+        _check_buf(t, name, (B, H, nblk), torch.float32, q8.device)
+    _check_buf(out, "out", q8.shape, torch.bfloat16, q8.device)
+    _check_buf(lse, "lse", (B, H, N), torch.float32, q8.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
@@ -178,6 +202,8 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
     if k.shape != v.shape or k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
         raise ValueError(f"k, v must be [B, H, Nk, d] matching q: {tuple(k.shape)} {tuple(v.shape)}")
     Nk = k.shape[2]
+    _check_buf(out, "out", q.shape, torch.bfloat16, q.device)
+    _check_buf(lse, "lse", (B, H, Nq), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if out is None else out
@@ -214,6 +240,8 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
     if lse is None or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) \
             or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_buf(t, name, q.shape, torch.bfloat16, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
