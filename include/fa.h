@@ -116,7 +116,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * s, or s * (1/sqrt(d)) with rotation.
  * Validation order: null x/x8/scales -> INVALID_ARG; B, H or N < 1 ->
  * INVALID_ARG; d not in {64, 96, 128, 256}, or signs given and d not a power
- * of two -> UNSUPPORTED; size limits -> TOO_LARGE; misaligned -> MISALIGNED;
+ * of two -> UNSUPPORTED; the size limits of fa_fwd -> TOO_LARGE; misaligned -> MISALIGNED;
  * launch error -> HIP.
  */
 int fa_quant_fp8(const void* x, void* x8, float* scales,
