@@ -102,7 +102,23 @@ def test_fwd_fp8_vs_emulator_and_exact(lib, d, causal):
     # The 5e-2 gate applies to the full-size FP8 workload (below); at these
     # small shapes the method itself (emulated) may sit slightly above it.
     assert e_gpu <= 1.5 * FP8_REL_RMSE
+    check_fp8_lse(lse_gpu, (qc, kc, vc), (sq, sk, sv), causal, scale)
+
+
+def check_fp8_lse(lse_gpu, codes, scales, causal, scale):
+    """The e4m3 kernel's LSE is the log-sum-exp of the scores of the
+    dequantised operands, except that its row sum adds the e4m3-rounded
+    probabilities the P V product used: each within 2^-4 of its value (3
+    mantissa bits, round to nearest), so the sum is within a factor
+    1 +- 2^-4 and the LSE within ln(1 + 2^-4) = 0.061 of the exact
+    log-sum-exp of the dequantised scores."""
+    qd, kd, vd = (fp8.dequantize(c, s) for c, s in zip(codes, scales))
+    _, lse_deq = attention(qd, kd, vd, causal, scale)
+    err = np.abs(lse_gpu - lse_deq)
+    announce("  lse vs dequantised oracle: max", float(err.max()), "mean", float(err.mean()))
     assert np.all(np.isfinite(lse_gpu))
+    assert float(err.max()) <= math.log1p(2.0 ** -4) + 1e-4
+    assert float(err.mean()) <= 1e-2
 
 
 @pytest.mark.parametrize("N", [1, 17, 65, 129, 300])
@@ -127,6 +143,36 @@ def test_fwd_fp8_ragged(lib, N, causal):
              "lse max abs", float(np.abs(lse_gpu - lse_ref).max()))
     assert e <= 2e-2
     assert rel_rmse(o_gpu, o_ref) <= 1.5 * FP8_REL_RMSE
+    check_fp8_lse(lse_gpu, (qc, kc, vc), (sq, sk, sv), causal, scale)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_scale_argument_and_optional_lse(lib, causal):
+    """A scale other than 1/sqrt(d) reaches the e4m3 kernel's scores (against
+    the emulator and the dequantised LSE with that scale), and skipping the
+    LSE store leaves O bit for bit unchanged."""
+    import torch
+    announce("fwd fp8 scale 0.05 / no lse", causal)
+    B, H, N, d = 1, 2, 300, 128
+    g = fa_inputs.make_qkv(B, H, N, d, 740, "outlier_replace")
+    signs = fa_inputs.random_signs(d, 741)
+    qc, sq = fp8.quantize(g.q, signs=signs)
+    kc, sk = fp8.quantize(g.k, signs=signs)
+    vc, sv = fp8.quantize(g.v)
+    scale = 0.05
+    o_gpu, lse_gpu = gpu_fwd_fp8(lib, (qc, kc, vc), (sq, sk, sv), causal, scale=scale)
+    o_emul = fp8.fp8_attention_emulate(qc, kc, vc, sq, sk, sv, causal, scale)
+    e = rel_rmse(o_gpu, o_emul)
+    announce("  gpu-vs-emulator", e)
+    assert e <= 2e-2
+    check_fp8_lse(lse_gpu, (qc, kc, vc), (sq, sk, sv), causal, scale)
+    dev = [torch.from_numpy(c).cuda().view(torch.float8_e4m3fn) for c in (qc, kc, vc)]
+    sc = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (sq, sk, sv)]
+    o1, l1 = lib.fwd_fp8(*dev, *sc, causal=causal, scale=scale)
+    o2, l2 = lib.fwd_fp8(*dev, *sc, causal=causal, scale=scale, return_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
 def test_fwd_fp8_causal_row0_closed_form(lib):
