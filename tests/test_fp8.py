@@ -271,3 +271,6 @@ def test_end_to_end_equals_explicit_pipeline(lib, d):
         torch.cuda.synchronize()
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
         assert torch.equal(l1, l2)
+        o3, l3 = lib.fwd(q, k, v, causal=causal, dtype=lib.FA_FP8_E4M3, return_lse=False)
+        torch.cuda.synchronize()
+        assert l3 is None and torch.equal(o1.view(torch.int16), o3.view(torch.int16))

@@ -100,3 +100,17 @@ def test_matches_fa_fwd_when_lengths_are_equal(lib):
     torch.cuda.synchronize()
     assert float((o1.float() - o2.float()).abs().max()) <= 2e-2
     assert float((l1 - l2).abs().max()) <= 1e-3
+
+
+def test_optional_lse(lib):
+    """Without an LSE output the merge skips its store and O is bit for bit
+    the same."""
+    import torch
+    announce("splitkv without lse 2 3 5 700 64 causal")
+    qb, kb, vb = make(2, 3, 5, 700, 64, 12004)
+    q, k, v = (fa_inputs.to_torch_bf16(x, "cuda") for x in (qb, kb, vb))
+    o1, l1 = lib.fwd_splitkv(q, k, v, causal=True, num_splits=3)
+    o2, l2 = lib.fwd_splitkv(q, k, v, causal=True, num_splits=3, return_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
