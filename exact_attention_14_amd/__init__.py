@@ -94,6 +94,15 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _launch(fn, name, device, *args):
+    """Calls a C entry point with the tensors' device current (the library
+    launches on the calling thread's current device) and that device's
+    current torch stream as the last argument; raises FAError on failure."""
+    import torch
+    with torch.cuda.device(device):
+        _check(fn(*args, _stream(device)), name)
+
+
 def _check_buf(t, name, shape, dtype, device):
     """A caller-provided output or side input must match exactly what the
     kernels read or write: contiguous, this dtype, shape and device."""
@@ -138,9 +147,8 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, dtype: int = 
     o = torch.empty_like(q) if out is None else out
     if lse is None and return_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
-                    float(scale), int(dtype), _stream(q.device))
-    _check(st, "fa_fwd")
+    _launch(lib.fa_fwd, "fa_fwd", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
+            d, int(bool(causal)), float(scale), int(dtype))
     return o, lse
 
 
@@ -158,9 +166,8 @@ def quant_fp8(x, per_tensor: bool = False, signs=None, out=None, scales=None):
     _check_buf(signs, "signs", (d,), torch.float32, x.device)
     x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device) if out is None else out
     sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device) if scales is None else scales
-    st = lib.fa_quant_fp8(_ptr(x), _ptr(x8), _ptr(sc), B, H, N, d, int(bool(per_tensor)),
-                          _ptr(signs), _stream(x.device))
-    _check(st, "fa_quant_fp8")
+    _launch(lib.fa_quant_fp8, "fa_quant_fp8", x.device, _ptr(x), _ptr(x8), _ptr(sc), B, H, N, d,
+            int(bool(per_tensor)), _ptr(signs))
     return x8, sc
 
 
@@ -181,10 +188,8 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = 
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
     if lse is None and return_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    st = lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv), _ptr(o),
-                        _ptr(lse), B, H, N, d, int(bool(causal)), float(scale),
-                        _stream(q8.device))
-    _check(st, "fa_fwd_fp8")
+    _launch(lib.fa_fwd_fp8, "fa_fwd_fp8", q8.device, _ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq),
+            _ptr(sk), _ptr(sv), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)), float(scale))
     return o, lse
 
 
@@ -209,9 +214,8 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
     o = torch.empty_like(q) if out is None else out
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    st = lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
-                            int(bool(causal)), float(scale), int(num_splits), _stream(q.device))
-    _check(st, "fa_fwd_splitkv")
+    _launch(lib.fa_fwd_splitkv, "fa_fwd_splitkv", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+            _ptr(lse), B, H, Nq, Nk, d, int(bool(causal)), float(scale), int(num_splits))
     return o, lse
 
 
@@ -247,9 +251,8 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                    _ptr(dv), B, H, N, d, int(bool(causal)), float(scale), _stream(q.device))
-    _check(st, "fa_bwd")
+    _launch(lib.fa_bwd, "fa_bwd", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+            _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)), float(scale))
     return dq, dk, dv
 
 
