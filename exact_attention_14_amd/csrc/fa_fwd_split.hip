@@ -280,6 +280,63 @@ __global__ __launch_bounds__(64) void split_combine_kernel(const float* __restri
   if (LSE != nullptr && cc == 0) LSE[r] = l > 0.f ? m + __logf(l) : -INFINITY;
 }
 
+// The merge for many splits: one workgroup per query row, kMergeGroups
+// groups of d/4 threads; group g merges splits g, g + kMergeGroups, ... with
+// a running maximum, then the groups' (max, sum, accumulator) are merged
+// through LDS by group 0. With one thread per (row, 4 columns) looping over
+// all splits, decode (few rows, 16-64 splits) left most of the GPU idle.
+constexpr int kMergeGroups = 8;
+
+template <int D>
+__global__ __launch_bounds__(kMergeGroups * D / 4) void split_combine_rows_kernel(
+    const float* __restrict__ Op, const float* __restrict__ Lp, u16* __restrict__ O,
+    float* __restrict__ LSE, int Nq, int splits) {
+  constexpr int C = D / 4;
+  constexpr int G = kMergeGroups;
+  __shared__ float sm[G][C], sl[G][C];
+  __shared__ f32x4 sa[G][C];
+  const long long r = blockIdx.x;
+  const int g = threadIdx.x / C, cc = threadIdx.x % C;
+  const long long bh = r / Nq;
+  const int i = (int)(r % Nq);
+  const size_t base = (size_t)bh * splits * Nq + i;  // split s at base + s*Nq
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = g; s < splits; s += G) {
+    const float ls = Lp[base + (size_t)s * Nq];
+    const f32x4 o = *(const f32x4*)(Op + (base + (size_t)s * Nq) * D + cc * 4);
+    const float m_new = fmaxf(m, ls);
+    const float f = m == m_new ? 1.f : __expf(m - m_new);  // m = -inf: f = 0
+    const float w = ls == -INFINITY ? 0.f : __expf(ls - m_new);
+    acc = acc * f + w * o;
+    l = l * f + w;
+    m = m_new;
+  }
+  sm[g][cc] = m;
+  sl[g][cc] = l;
+  sa[g][cc] = acc;
+  __syncthreads();
+  if (g != 0) return;
+  float mm = sm[0][cc];
+#pragma unroll
+  for (int x = 1; x < G; ++x) mm = fmaxf(mm, sm[x][cc]);
+  float ll = 0.f;
+  f32x4 aa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int x = 0; x < G; ++x) {
+    const float w = sm[x][cc] == -INFINITY ? 0.f : __expf(sm[x][cc] - mm);
+    ll += w * sl[x][cc];
+    aa += w * sa[x][cc];
+  }
+  const float inv = ll > 0.f ? 1.f / ll : 0.f;
+  bf16x4 out;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) out[x] = (__bf16)(aa[x] * inv);
+  *(bf16x4*)(O + r * D + cc * 4) = out;
+  if (LSE != nullptr && cc == 0) LSE[r] = ll > 0.f ? mm + __logf(ll) : -INFINITY;
+}
+
 template <int D, bool CAUSAL, int NW, int KT, int S>
 hipError_t split_launch(const void* q, const void* k, const void* v, void* o, float* lse,
                         float* ws, int B, int H, int Nq, int Nk, int splits, float scale,
@@ -297,6 +354,12 @@ hipError_t split_launch(const void* q, const void* k, const void* v, void* o, fl
   hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL, NW, KT, S>), dim3((unsigned)nwg), dim3(64 * NW), 0,
                      stream, (const u16*)q, (const u16*)k, (const u16*)v, op, lp, Nq, Nk, nqt,
                      splits, tps, (int)nwg, scale);
+  if (splits >= kMergeGroups) {
+    hipLaunchKernelGGL((split_combine_rows_kernel<D>), dim3((unsigned)rows),
+                       dim3(kMergeGroups * D / 4), 0, stream, (const float*)op, (const float*)lp,
+                       (u16*)o, lse, Nq, splits);
+    return hipGetLastError();
+  }
   const long long threads = rows * (D / 4);
   hipLaunchKernelGGL((split_combine_kernel<D>), dim3((unsigned)((threads + 63) / 64)),
                      dim3(64), 0, stream, (const float*)op, (const float*)lp, (u16*)o, lse, rows,
@@ -344,10 +407,13 @@ int split_count(int B, int H, int Nq, int Nk, int requested) {
 
 long long split_work_items(int B, int H, int Nq, int d, int splits) {
   // Split kernel: one wave per 32 queries (Nq <= 32) or four per 128; the
-  // merge: d/4 threads per query row in 64-thread workgroups.
+  // merge: d/4 threads per query row in 64-thread workgroups, or, with at
+  // least kMergeGroups splits, kMergeGroups * d/4 threads per row.
   const int nw = Nq <= 32 ? 1 : 4;
   const long long split_items = (long long)B * H * ((Nq + 32 * nw - 1) / (32 * nw)) * splits * 64 * nw;
-  const long long merge_items = ((long long)B * H * Nq * (d / 4) + 63) / 64 * 64;
+  const long long rows = (long long)B * H * Nq;
+  const long long merge_items = splits >= kMergeGroups ? rows * kMergeGroups * (d / 4)
+                                                       : (rows * (d / 4) + 63) / 64 * 64;
   return split_items > merge_items ? split_items : merge_items;
 }
 
