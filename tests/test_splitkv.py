@@ -64,6 +64,10 @@ CASES = [
     (1, 1, 1, 1, 64, True, 0),          # one key
     (1, 2, 5, 130, 96, False, 64),      # more splits requested than tiles
     (1, 2, 100, 100, 64, False, 0),
+    # 8 or more splits (one workgroup per row in the merge): early causal rows
+    # have whole splits without a visible key; 13 splits over 8 merge groups
+    (1, 2, 1664, 1664, 64, True, 13),
+    (2, 2, 3, 2000, 96, False, 9),
 ]
 
 
