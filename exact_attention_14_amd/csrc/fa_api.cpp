@@ -207,8 +207,6 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (!(scale > 0.f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   int st = sizes_check(B, H, N, d);
   if (st != FA_OK) return st;
-  // The row-term pass runs four threads per row.
-  if ((long long)B * H * N * 4 > kMaxWorkItems - 255) return FA_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_MISALIGNED;

@@ -5,13 +5,16 @@
 // pass beside the forward): with P = softmax(scale * Q K^T) recomputed tile by
 // tile from the forward's per-row log-sum-exp (no running maximum is needed
 // on the way back),
-//   D_i  = sum_c dO_ic O_ic                (pre-pass, = sum_j P_ij dP_ij)
+//   D_i  = sum_c dO_ic O_ic                (= sum_j P_ij dP_ij)
 //   dV   = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
 //   dQ   = scale * dS K,  dK = scale * dS^T Q.
 // The N x N matrices never leave the chip. Two kernels share the work without
-// atomics (results are deterministic): one owns a tile of keys and sweeps the
-// query tiles for dK and dV, the other owns a tile of queries and sweeps the
-// key tiles for dQ; both recompute S and dP.
+// atomics (results are deterministic): one owns a tile of queries and sweeps
+// the key tiles for dQ, the other owns a tile of keys and sweeps the query
+// tiles for dK and dV; both recompute S and dP. The dQ kernel runs first and
+// also forms each of its rows' D and -LSE log2(e), which the dK/dV kernel
+// then streams (a separate pass over O and dO for them cost a launch and
+// about 11 us at B=4 H=16 N=2048 d=128).
 //
 // gfx950 mapping (same building blocks as the forward kernel)
 //   * dK/dV: each lane owns one key. K and V stay in registers as the B
@@ -34,46 +37,6 @@
 
 namespace fa {
 namespace {
-
-// --------------------------------------------------------------- pre-pass ---
-
-// Per-row terms of the backward pass:
-//   Dout[r]  = sum_c dO[r][c] * O[r][c]   (float32 sums of bf16 products)
-//   NLout[r] = -LSE[r] * log2(e)          (P = exp2(scale log2(e) S + NL))
-// Four lanes per row, each summing D/32 16-byte chunks (chunk c*4 + lane of
-// the row, so that a wave's loads cover 64 contiguous bytes of 16 rows),
-// then a two-step butterfly.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_rows_kernel(const u16* __restrict__ O,
-                                                       const u16* __restrict__ dO,
-                                                       const float* __restrict__ LSE,
-                                                       float* __restrict__ Dout,
-                                                       float* __restrict__ NLout, long long rows) {
-  constexpr int C = D / 32;
-  const long long r = ((long long)blockIdx.x * 256 + threadIdx.x) >> 2;
-  const int j = threadIdx.x & 3;
-  float acc = 0.f;
-  if (r < rows) {
-    const uint4* o = (const uint4*)(O + r * D);
-    const uint4* g = (const uint4*)(dO + r * D);
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const uint4 a = o[c * 4 + j], b = g[c * 4 + j];
-      const u16* ea = (const u16*)&a;
-      const u16* eb = (const u16*)&b;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        acc = fmaf(__uint_as_float((unsigned)ea[e] << 16), __uint_as_float((unsigned)eb[e] << 16),
-                   acc);
-    }
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  if (r < rows && j == 0) {
-    Dout[r] = acc;
-    NLout[r] = -LSE[r] * kLog2e;
-  }
-}
 
 // 4-byte HBM -> LDS copy per lane (lane l writes lds + 4 l), written as
 // assembly for the same reason as the 16-byte tile copies: the kernel's own
@@ -336,8 +299,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSi
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    const u16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
-    u16* __restrict__ dQ, int N, int ntq, int nwg, int hpx, float scale) {
+    const u16* __restrict__ dO, const u16* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ NL, float* __restrict__ Dvec, u16* __restrict__ dQ, int N, int ntq,
+    int nwg, int hpx, float scale) {
   using G = Geo<D>;
   using CP = TileCopy<D, 4>;
   __shared__ __attribute__((aligned(1024))) char ks0[G::TILEB];
@@ -373,11 +337,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSi
   bf16x8 qreg[G::NK], greg[G::NK];
   load_own_rows<D>(make_rsrc(Q + head * D, head_bytes), qi, half, qreg);
   load_own_rows<D>(make_rsrc(dO + head * D, head_bytes), qi, half, greg);
+  // The row terms of the lane's query: D = sum_c dO O (this half-wave's
+  // columns, then the other half's through lane ^ 32) and -LSE log2(e).
   // Queries past N read zeros (their rows are dropped at the store).
-  const float nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-      make_rsrc(NL + head, (unsigned)N * 4u), (unsigned)qi * 4u, 0, 0));
-  const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-      make_rsrc(Dvec + head, (unsigned)N * 4u), (unsigned)qi * 4u, 0, 0));
+  float dd;
+  {
+    bf16x8 oreg[G::NK];
+    load_own_rows<D>(make_rsrc(O + head * D, head_bytes), qi, half, oreg);
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < G::NK; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part = fmaf((float)greg[kk][j], (float)oreg[kk][j], part);
+    dd = part + __shfl_xor(part, 32);
+  }
+  const float nl = -__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                       make_rsrc(LSE + head, (unsigned)N * 4u), (unsigned)qi * 4u, 0, 0)) *
+                   kLog2e;
+  // Published for the dK/dV kernel, one lane per row (the second half-wave
+  // and rows past N fall outside the buffer range and are dropped).
+  {
+    const unsigned so = half == 0 ? (unsigned)qi * 4u : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(nl),
+                                          make_rsrc(NL + head, (unsigned)N * 4u), so, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dd),
+                                          make_rsrc(Dvec + head, (unsigned)N * 4u), so, 0, 0);
+  }
   const Offsets<D> off(lane);
 
   f32x16 dq[G::NO];
@@ -454,19 +439,19 @@ hipError_t bwd_launch(const void* q, const void* k, const void* v, const void* o
   const long long rows = (long long)B * H * N;
   float* const dvec = ws;
   float* const nl = ws + rows;
-  hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3((unsigned)((rows * 4 + 255) / 256)), dim3(256), 0,
-                     stream, (const u16*)o, (const u16*)dout, lse, dvec, nl, rows);
   const int nt = (N + 127) / 128;
   const long long nwg = (long long)nt * B * H;
   if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
   const int hpx = ((long long)B * H) % 8 == 0 ? (int)(((long long)B * H) / 8) : 0;
+  // dQ first: it also writes the row terms D and -LSE log2(e) that the
+  // dK/dV kernel reads (stream order makes them visible to it).
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream,
+                     (const u16*)q, (const u16*)k, (const u16*)v, (const u16*)dout, (const u16*)o,
+                     lse, nl, dvec, (u16*)dq, N, nt, (int)nwg, hpx, scale);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream,
                      (const u16*)q, (const u16*)k, (const u16*)v, (const u16*)dout,
                      (const float*)nl, (const float*)dvec, (u16*)dk, (u16*)dv, N, nt, (int)nwg,
                      hpx, scale);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream,
-                     (const u16*)q, (const u16*)k, (const u16*)v, (const u16*)dout,
-                     (const float*)nl, (const float*)dvec, (u16*)dq, N, nt, (int)nwg, hpx, scale);
   return hipGetLastError();
 }
 

@@ -173,11 +173,10 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
  * Scratch: 2 * B*H*N floats, stream-ordered from the library's pool.
  * Validation order: null q/k/v/o/lse/dout/dq/dk/dv -> INVALID_ARG; B, H or
  * N < 1 -> INVALID_ARG; d not in {64, 96, 128, 256} -> UNSUPPORTED; scale not
- * finite and > 0 -> INVALID_ARG; N*d > 2^30, B*H >= 2^31,
- * B*H*ceil(N/128) >= 2^24 or B*H*N >= 2^30 (the grid limit of 2^32 - 1
- * work-items; four threads per row in the row-term pass) -> TOO_LARGE; a
- * pointer not 16-byte aligned -> MISALIGNED; launch or scratch allocation
- * error -> HIP.
+ * finite and > 0 -> INVALID_ARG; N*d > 2^30, B*H >= 2^31 or
+ * B*H*ceil(N/128) >= 2^24 (the grid limit of 2^32 - 1 work-items) ->
+ * TOO_LARGE; a pointer not 16-byte aligned -> MISALIGNED; launch or scratch
+ * allocation error -> HIP.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -118,9 +118,8 @@ def test_bwd_validation_order(lib):
     assert call(scale=float("nan")) == lib.FA_ERR_INVALID_ARG
     assert call(N=1 << 24, d=128) == lib.FA_ERR_TOO_LARGE
     assert call(B=1 << 12, H=1 << 12, N=1) == lib.FA_ERR_TOO_LARGE
-    # 2^30 rows: the row-term pass would need 2^32 threads (the tile grid fits)
-    assert call(B=1 << 10, H=1 << 10, N=1 << 10, d=64) == lib.FA_ERR_TOO_LARGE
-    assert call(B=1 << 10, H=(1 << 10) - 1, N=1 << 10, d=64, dq=P + 2) == lib.FA_ERR_MISALIGNED
+    # just below the tile-grid limit the size check passes and the next check decides
+    assert call(B=1 << 12, H=(1 << 12) - 1, N=128, d=64, dq=P + 2) == lib.FA_ERR_MISALIGNED
     for name in ("q", "o", "lse", "do", "dv"):
         assert call(**{name: P + 4}) == lib.FA_ERR_MISALIGNED, name
     # earlier checks win over later ones
