@@ -274,3 +274,17 @@ def test_end_to_end_equals_explicit_pipeline(lib, d):
         o3, l3 = lib.fwd(q, k, v, causal=causal, dtype=lib.FA_FP8_E4M3, return_lse=False)
         torch.cuda.synchronize()
         assert l3 is None and torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
+def test_fp8_deterministic(lib):
+    """Repeated end-to-end FP8 calls (quantisation passes, in-kernel Q
+    quantisation, e4m3 forward) give bitwise identical outputs."""
+    import torch
+    announce("fp8 determinism 2 4 1000 128 causal")
+    g = fa_inputs.make_qkv(2, 4, 1000, 128, 750, "outlier_replace")
+    q, k, v = (fa_inputs.to_torch_bf16(b, "cuda") for b in (g.q_bits, g.k_bits, g.v_bits))
+    runs = [lib.fwd(q, k, v, causal=True, dtype=lib.FA_FP8_E4M3) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, lse in runs[1:]:
+        assert torch.equal(o.view(torch.int16), runs[0][0].view(torch.int16))
+        assert torch.equal(lse, runs[0][1])

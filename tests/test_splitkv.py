@@ -118,3 +118,17 @@ def test_optional_lse(lib):
     torch.cuda.synchronize()
     assert l2 is None
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_deterministic(lib):
+    """Repeated calls give bitwise identical outputs (fixed split boundaries
+    and merge order)."""
+    import torch
+    announce("splitkv determinism 2 4 16 5000 128 causal")
+    qb, kb, vb = make(2, 4, 16, 5000, 128, 12005)
+    q, k, v = (fa_inputs.to_torch_bf16(x, "cuda") for x in (qb, kb, vb))
+    runs = [lib.fwd_splitkv(q, k, v, causal=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, lse in runs[1:]:
+        assert torch.equal(o.view(torch.int16), runs[0][0].view(torch.int16))
+        assert torch.equal(lse, runs[0][1])
