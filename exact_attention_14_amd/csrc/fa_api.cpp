@@ -120,9 +120,7 @@ int run_fp8_path(const void* q, const void* k, const void* v, void* o, float* ls
   float* sk = reinterpret_cast<float*>(base + 2 * t_bytes);
   float* sv = reinterpret_cast<float*>(base + 2 * t_bytes + s_bytes);
   float* signs = reinterpret_cast<float*>(base + 2 * t_bytes + 2 * s_bytes);
-  e = fa::launch_fill_signs(signs, d, kSignKey, stream);
-  if (e == hipSuccess) e = fa::launch_quant_fp8(k, k8, sk, B, H, N, d, false, signs, stream);
-  if (e == hipSuccess) e = fa::launch_quant_fp8(v, v8, sv, B, H, N, d, false, nullptr, stream);
+  e = fa::launch_quant_kv_fp8(k, v, k8, v8, sk, sv, signs, kSignKey, B, H, N, d, stream);
   if (e == hipSuccess)
     e = fa::launch_fwd_fp8_qbf16(q, signs, k8, v8, sk, sv, o, lse, B, H, N, d, causal != 0, scale,
                                  stream);

@@ -33,9 +33,10 @@ __device__ __forceinline__ unsigned long long splitmix64(unsigned long long x) {
   return x ^ (x >> 31);
 }
 
-__global__ void fill_signs_kernel(float* signs, int d, unsigned long long key) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < d) signs[i] = (splitmix64(key + (unsigned long long)i) >> 63) ? -1.f : 1.f;
+// Sign i of the rotation with this key: -1 where the top bit of
+// SplitMix64(key + i) is set, else +1.
+__device__ __forceinline__ float sign_of(unsigned long long key, int i) {
+  return (splitmix64(key + (unsigned long long)i) >> 63) ? -1.f : 1.f;
 }
 
 // ----------------------------------------------------------- quantiser ------
@@ -193,6 +194,53 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const u16* __restrict__ 
   });
   if constexpr (MODE == kGivenAmax) __syncthreads();  // every thread has read scales[sidx]
   if (tid == 0) scales[sidx] = ROTATE ? s * rsqrt_d : s;
+}
+
+// The K and V passes of the end-to-end FP8 path in one launch: blockIdx.y = 0
+// quantises K's blocks rotated by the signs of `key` (each workgroup makes
+// them in LDS; workgroup (0, 0) also stores them for the forward kernel, which
+// quantises Q with the same signs), blockIdx.y = 1 quantises V's blocks
+// without rotation. Per block the arithmetic is quant_fp8_kernel's, so the
+// codes and scales equal those of two quant_fp8_kernel launches bit for bit.
+template <int D>
+__global__ __launch_bounds__(256) void quant_kv_fp8_kernel(
+    const u16* __restrict__ K, const u16* __restrict__ V, uint8_t* __restrict__ K8,
+    uint8_t* __restrict__ V8, float* __restrict__ SK, float* __restrict__ SV,
+    float* __restrict__ signs_out, unsigned long long key, int N, int nblk, float rsqrt_d) {
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x % nblk;
+  const size_t bh = blockIdx.x / nblk;
+  const int row0 = blk * kBlock;
+  const size_t sidx = bh * nblk + blk;
+  const unsigned nbytes = (unsigned)N * D * 2u;
+  __shared__ float red[4];
+  if (blockIdx.y == 0) {
+    __shared__ float sgn[D];
+    for (int i = tid; i < D; i += 256) {
+      sgn[i] = sign_of(key, i);
+      if (blockIdx.x == 0) signs_out[i] = sgn[i];
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(K + bh * (size_t)N * D, nbytes);
+    const __amdgpu_buffer_rsrc_t rx8 = make_rsrc(K8 + bh * (size_t)N * D, (unsigned)N * D);
+    BlockQuant<D, true> bq;
+    const float s = block_scale(block_max(bq.load(rx, row0, sgn, tid), red, tid));
+    bq.emit(1.f / s, tid, [&](int row, int ch, i32x2 packed) {
+      __builtin_amdgcn_raw_buffer_store_b64(packed, rx8, (unsigned)((row0 + row) * D + ch * 8), 0,
+                                            0);
+    });
+    if (tid == 0) SK[sidx] = s * rsqrt_d;
+  } else {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(V + bh * (size_t)N * D, nbytes);
+    const __amdgpu_buffer_rsrc_t rx8 = make_rsrc(V8 + bh * (size_t)N * D, (unsigned)N * D);
+    BlockQuant<D, false> bq;
+    const float s = block_scale(block_max(bq.load(rx, row0, nullptr, tid), red, tid));
+    bq.emit(1.f / s, tid, [&](int row, int ch, i32x2 packed) {
+      __builtin_amdgcn_raw_buffer_store_b64(packed, rx8, (unsigned)((row0 + row) * D + ch * 8), 0,
+                                            0);
+    });
+    if (tid == 0) SV[sidx] = s;
+  }
 }
 
 // Maximum over all block maxima, written back to every entry.
@@ -652,10 +700,27 @@ hipError_t fwd_launch(const void* q8, const void* k8, const void* v8, const floa
 
 }  // namespace
 
-hipError_t launch_fill_signs(float* signs, int d, unsigned long long key, hipStream_t stream) {
-  hipLaunchKernelGGL(fill_signs_kernel, dim3((d + 255) / 256), dim3(256), 0, stream, signs, d,
-                     key);
-  return hipGetLastError();
+hipError_t launch_quant_kv_fp8(const void* k, const void* v, void* k8, void* v8, float* sk,
+                               float* sv, float* signs, unsigned long long key, int B, int H,
+                               int N, int d, hipStream_t stream) {
+  const int nblk = (N + kBlock - 1) / kBlock;
+  const long long ngrid = (long long)nblk * B * H;
+  if (ngrid >= (1LL << 31)) return hipErrorInvalidValue;
+  const float rsqrt_d = (float)(1.0 / sqrt((double)d));
+#define FA_CASE(DD)                                                                         \
+  case DD:                                                                                  \
+    hipLaunchKernelGGL((quant_kv_fp8_kernel<DD>), dim3((unsigned)ngrid, 2), dim3(256), 0,   \
+                       stream, (const u16*)k, (const u16*)v, (uint8_t*)k8, (uint8_t*)v8, sk, \
+                       sv, signs, key, N, nblk, rsqrt_d);                                   \
+    return hipGetLastError();
+  switch (d) {
+    FA_CASE(64)
+    FA_CASE(128)
+    FA_CASE(256)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef FA_CASE
 }
 
 hipError_t launch_quant_fp8(const void* x, void* x8, float* scales, int B, int H, int N, int d,

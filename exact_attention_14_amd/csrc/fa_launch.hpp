@@ -47,8 +47,11 @@ hipError_t launch_fwd_fp8_qbf16(const void* qbf, const float* signs, const void*
                                 float* lse, int B, int H, int N, int d, bool causal, float scale,
                                 hipStream_t stream);
 
-// Writes d random signs (+-1) derived from a fixed 64-bit key.
-hipError_t launch_fill_signs(float* signs, int d, unsigned long long key,
-                             hipStream_t stream);
+// The end-to-end FP8 path's K and V passes in one launch: K rotated by the
+// signs of `key` (also written to `signs`, d floats), V not rotated; codes and
+// scales as two launch_quant_fp8 calls would give.
+hipError_t launch_quant_kv_fp8(const void* k, const void* v, void* k8, void* v8, float* sk,
+                               float* sv, float* signs, unsigned long long key, int B, int H,
+                               int N, int d, hipStream_t stream);
 
 }  // namespace fa
