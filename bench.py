@@ -146,10 +146,6 @@ def extras(fa, only=None):
                "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / PEAK_HBM, 1),
                "bound": "hbm" if fl / nbytes < RIDGE_BF16 else "mfma"}
-        if Nq == Nk:  # the same problem through fa_fwd, for comparison
-            ms2 = time_calls(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse), steps, 3)
-            rec["fa_fwd_ms"] = round(ms2, 4)
-            rec["fa_fwd_tflops"] = round(fl / (ms2 * 1e-3) / 1e12, 1)
         out.append(rec)
         del q, k, v, o, lse
 

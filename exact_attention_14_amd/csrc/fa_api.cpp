@@ -129,6 +129,34 @@ int run_fp8_path(const void* q, const void* k, const void* v, void* o, float* ls
   return hip_status(ef, "hipFreeAsync");
 }
 
+// The split-KV forward into stream-ordered scratch (the partial outputs and
+// log-sum-exps of the splits); `splits` is already the normalised count.
+int run_split_path(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int Nq, int Nk, int d, int causal, float scale, int splits,
+                   hipStream_t s) {
+  void* ws = nullptr;
+  hipError_t e = scratch_alloc(&ws, (size_t)splits * B * H * Nq * (d + 1) * sizeof(float), s);
+  if (e != hipSuccess) return hip_status(e, "scratch allocation");
+  e = fa::launch_fwd_split_bf16(q, k, v, o, lse, static_cast<float*>(ws), B, H, Nq, Nk, d,
+                                causal != 0, splits, scale, s);
+  hipError_t ef = hipFreeAsync(ws, s);
+  if (e != hipSuccess) return hip_status(e, "fwd_split launch");
+  return hip_status(ef, "hipFreeAsync");
+}
+
+// bf16 self-attention with fewer than 256 query-tile workgroups (few heads)
+// and at least 2048 keys leaves compute units idle; the key axis then
+// supplies the parallelism: such calls take the split-KV path (the same
+// products and online softmax, partial results merged by LSE). Returns the
+// split count to use, or 0 for the one-pass kernel.
+int fwd_splits_for(int B, int H, int N, int d) {
+  if (!split_dim_ok(d) || N < 2048 || (long long)N * d > (1LL << 29)) return 0;
+  if ((long long)B * H * ((N + 127) / 128) >= 256) return 0;
+  const int splits = fa::split_count(B, H, N, N, 0);
+  if (splits < 2 || fa::split_work_items(B, H, N, d, splits) > kMaxWorkItems) return 0;
+  return splits;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,9 +182,12 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (log_enabled())
     std::fprintf(stderr, "[fa] fa_fwd dtype=%d B=%d H=%d N=%d d=%d causal=%d scale=%g\n", dtype,
                  B, H, N, d, causal, (double)scale);
-  if (dtype == FA_BF16)
+  if (dtype == FA_BF16) {
+    const int splits = fwd_splits_for(B, H, N, d);
+    if (splits > 0) return run_split_path(q, k, v, o, lse, B, H, N, N, d, causal, scale, splits, s);
     return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal != 0, scale, s),
                       "fwd_bf16 launch");
+  }
   return run_fp8_path(q, k, v, o, lse, B, H, N, d, causal, scale, s);
 }
 
@@ -243,15 +274,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   if (log_enabled())
     std::fprintf(stderr, "[fa] fa_fwd_splitkv B=%d H=%d Nq=%d Nk=%d d=%d causal=%d splits=%d\n", B,
                  H, Nq, Nk, d, causal, splits);
-  // Stream-ordered scratch: the partial outputs and log-sum-exps of the splits.
-  void* ws = nullptr;
-  hipError_t e = scratch_alloc(&ws, (size_t)splits * B * H * Nq * (d + 1) * sizeof(float), s);
-  if (e != hipSuccess) return hip_status(e, "scratch allocation");
-  e = fa::launch_fwd_split_bf16(q, k, v, o, lse, static_cast<float*>(ws), B, H, Nq, Nk, d,
-                                causal != 0, splits, scale, s);
-  hipError_t ef = hipFreeAsync(ws, s);
-  if (e != hipSuccess) return hip_status(e, "fwd_split launch");
-  return hip_status(ef, "hipFreeAsync");
+  return run_split_path(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, splits, s);
 }
 
 int fa_splitkv_splits(int B, int H, int Nq, int Nk, int num_splits) {
