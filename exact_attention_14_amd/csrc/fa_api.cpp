@@ -144,14 +144,19 @@ int run_split_path(const void* q, const void* k, const void* v, void* o, float* 
   return hip_status(ef, "hipFreeAsync");
 }
 
-// bf16 self-attention with fewer than 256 query-tile workgroups (few heads)
-// and at least 2048 keys leaves compute units idle; the key axis then
-// supplies the parallelism: such calls take the split-KV path (the same
-// products and online softmax, partial results merged by LSE). Returns the
-// split count to use, or 0 for the one-pass kernel.
+// bf16 self-attention with at most 128 query-tile workgroups (half the
+// compute units) and at least 4096 keys leaves the GPU half idle; the key
+// axis then supplies the parallelism: such calls take the split-KV path (the
+// same products and online softmax, partial results merged by LSE). Measured
+// against the one-pass kernel at d = 128: +8 to +55% at 128 workgroups; from
+// 160 to 240 workgroups the one-pass kernel was faster non-causal (by
+// 20-45%), so those stay on it, as does d = 64 (the one-pass kernel runs
+// three waves per SIMD there: -10% non-causal at 128 workgroups) and d = 96
+// (not measured). Returns the split count to use, or 0 for the one-pass
+// kernel.
 int fwd_splits_for(int B, int H, int N, int d) {
-  if (!split_dim_ok(d) || N < 2048 || (long long)N * d > (1LL << 29)) return 0;
-  if ((long long)B * H * ((N + 127) / 128) >= 256) return 0;
+  if (d != 128 || N < 4096 || (long long)N * d > (1LL << 29)) return 0;
+  if ((long long)B * H * ((N + 127) / 128) > 128) return 0;
   const int splits = fa::split_count(B, H, N, N, 0);
   if (splits < 2 || fa::split_work_items(B, H, N, d, splits) > kMaxWorkItems) return 0;
   return splits;

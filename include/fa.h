@@ -72,9 +72,9 @@ typedef enum fa_status {
  * lse     : float32 [B, H, N] or NULL         scale : softmax scale, finite > 0
  *           (callers normally pass 1/sqrt(d), the equation's scaling)
  * d       : 64, 96, 128 or 256 for FA_BF16; 64, 128 or 256 for FA_FP8_E4M3
- * dtype   : FA_BF16 runs the bf16 matrix-core path. With fewer than 256
- *           query tiles in all (B*H*ceil(N/128) < 256), N >= 2048 and
- *           d <= 128 it runs the split-KV path of fa_fwd_splitkv (automatic
+ * dtype   : FA_BF16 runs the bf16 matrix-core path. With at most 128
+ *           query tiles in all (B*H*ceil(N/128) <= 128), N >= 4096 and
+ *           d = 128 it runs the split-KV path of fa_fwd_splitkv (automatic
  *           split count; stream-ordered scratch from the library's pool):
  *           the same products and softmax, partial results merged by LSE,
  *           so the output differs from the one-pass kernel's only by

@@ -182,17 +182,17 @@ def test_random_shapes(lib, case):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_few_heads_long_sequence(lib, causal):
-    """Fewer than 256 query-tile workgroups and N >= 2048: fa_fwd takes the
-    split-KV path (key axis split, partials merged by LSE). Full parity with
-    the oracle, and the same bits as fa_fwd_splitkv with automatic splits;
-    d = 256 (no split-KV kernel) keeps the one-pass kernel."""
+    """At most 128 query-tile workgroups, N >= 4096 and d = 128: fa_fwd takes
+    the split-KV path (key axis split, partials merged by LSE). Full parity
+    with the oracle, and the same bits as fa_fwd_splitkv with automatic
+    splits; the same sizes at d = 64, 96 and 256 keep the one-pass kernel."""
     import torch
-    check_full(lib, 1, 2, 2048, 128, causal, 20000 + causal)
-    g = fa_inputs.make_qkv(1, 3, 2304, 96, 20002)
+    check_full(lib, 1, 2, 4096, 128, causal, 20000 + causal)
+    g = fa_inputs.make_qkv(1, 3, 4096, 128, 20002)
     q, k, v = (fa_inputs.to_torch_bf16(b, "cuda") for b in (g.q_bits, g.k_bits, g.v_bits))
     o1, l1 = lib.fwd(q, k, v, causal=causal)
     o2, l2 = lib.fwd_splitkv(q, k, v, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
-    check_sampled(lib, 1, 3, 2304, 96, causal, 20002)
-    check_full(lib, 1, 1, 2048, 256, causal, 20003)
+    for d in (64, 96, 256):
+        check_sampled(lib, 1, 3, 4096, d, causal, 20002 + d)
