@@ -82,11 +82,11 @@ typedef enum fa_status {
  *           FA_FP8_E4M3 runs the FP8 path end to end on bf16 inputs: Q and K
  *           are rotated by a fixed random-sign Hadamard matrix and all three
  *           are block-quantised to e4m3, then the fa_fwd_fp8 kernel runs.
- *           K and V go through fa_quant_fp8 into stream-ordered scratch
- *           (the library's pool, on `stream`); each workgroup of the
- *           forward kernel quantises its own 128-row Q block with the same
- *           arithmetic, so the output equals fa_quant_fp8 + fa_fwd_fp8 bit
- *           for bit. The fixed signs: sign i is -1 where the top bit of
+ *           K and V are quantised in one launch (fa_quant_fp8's arithmetic)
+ *           into stream-ordered scratch (the library's pool, on `stream`);
+ *           each workgroup of the forward kernel quantises its own 128-row
+ *           Q block with the same arithmetic, so the output equals
+ *           fa_quant_fp8 + fa_fwd_fp8 bit for bit. The fixed signs: sign i is -1 where the top bit of
  *           SplitMix64(0x5A17C0DE + i) is set, else +1 (SplitMix64: Steele,
  *           Lea, Flood 2014; the state is incremented by the golden gamma
  *           before mixing). d must be a power of two.
