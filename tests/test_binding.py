@@ -52,3 +52,36 @@ def test_wrong_buffers_are_refused(lib):
     with pytest.raises(ValueError):
         lib.fwd_fp8(q8, k8, v8, sq, sk, sv, out=bad_o[0])
     torch.cuda.synchronize()
+
+
+def test_side_streams_and_scratch_pool(lib):
+    """Calls enqueue on the caller's current stream: the same inputs run on
+    two side streams at once (FP8 end to end, backward and split-KV, which
+    take stream-ordered scratch from the library's pool) give the bits of a
+    run on the default stream."""
+    import torch
+    import fa_inputs
+    g = fa_inputs.make_qkv(2, 4, 1000, 128, 760)
+    q, k, v = (fa_inputs.to_torch_bf16(b, "cuda") for b in (g.q_bits, g.k_bits, g.v_bits))
+    do = torch.randn_like(q)
+
+    def run():
+        o8, l8 = lib.fwd(q, k, v, causal=True, dtype=lib.FA_FP8_E4M3)
+        o, lse = lib.fwd(q, k, v, causal=True)
+        grads = lib.bwd(q, k, v, o, lse, do, causal=True)
+        os_, ls = lib.fwd_splitkv(q[:, :, -7:].contiguous(), k, v, causal=True)
+        return (o8, l8, o, lse, *grads, os_, ls)
+
+    ref = run()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            outs.append(run())
+    torch.cuda.synchronize()
+    for res in outs:
+        for a, b in zip(res, ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
