@@ -78,14 +78,42 @@ __device__ __forceinline__ float lane_xor(float v, int m) {
 
 // The arithmetic of one 128-row block, shared by the quantisation pass and
 // the e4m3 forward kernel's quantisation of its own Q block (both therefore
-// give bit-identical codes and scales). 256 threads; thread tid holds chunks
-// cid = k*256 + tid (row cid / CPR, 8 columns from 8 * (cid % CPR)).
-template <int D, bool ROTATE>
+// give bit-identical codes and scales). 256 threads. With GR = 1 thread tid
+// holds one 8-column chunk in each of NC rows (consecutive lanes, consecutive
+// chunks: the loads of a wave cover whole rows). With rotation and GR = 4 it
+// holds 4 consecutive chunks (32 columns) of each of NC/4 rows, so the
+// Walsh-Hadamard butterflies of strides 1..16 run in registers and only
+// strides >= 32 cross lanes (D/32 lanes per row): about 17% fewer VALU
+// instructions, but each load instruction of a wave touches 4x as many cache
+// lines. The quantisation passes are bound by memory access and keep GR = 1
+// (GR = 4 measured 7-19% slower there); the forward kernel's quantisation of
+// its own Q block is bound by instruction latency and uses GR = 4 (+1.5 to
+// +2.5% end to end). Either way the butterflies are the same pairs in the
+// same order (strides 1, 2, 4, ..., D/2), so the values do not depend on the
+// layout.
+template <int D, bool ROTATE, int GR = 1>
 struct BlockQuant {
-  static constexpr int CPR = D / 8;
-  static constexpr int NC = kBlock * CPR / 256;  // chunks per thread
-  static_assert(!ROTATE || (64 % CPR == 0), "rotation needs a row inside one wave");
+  static constexpr int CPR = D / 8;                // 8-column chunks per row
+  static constexpr int NC = kBlock * CPR / 256;    // chunks per thread
+  static constexpr int G = ROTATE ? GR : 1;        // consecutive chunks of a row per thread
+  static constexpr int L = CPR / G;                // lanes per row
+  static constexpr int RPT = NC / G;               // rows per thread
+  static constexpr int RSTEP = 256 / L;            // rows between a thread's rows (G > 1)
+  static_assert(NC % G == 0 && CPR % G == 0, "chunk groups tile the block");
+  static_assert(!ROTATE || 64 % L == 0, "a row's lanes sit in one wave");
   float x[NC][8];
+
+  // Row and chunk of the thread's chunk r * G + gi. One chunk per row: chunk
+  // cid = r * 256 + tid of the block (consecutive lanes, consecutive chunks;
+  // also when 256 is not a multiple of CPR, as for d = 96).
+  __device__ __forceinline__ int row_of(int r, int tid) const {
+    if constexpr (G == 1) return (r * 256 + tid) / CPR;
+    else return r * RSTEP + tid / L;
+  }
+  __device__ __forceinline__ int chunk_of(int r, int gi, int tid) const {
+    if constexpr (G == 1) return (r * 256 + tid) % CPR;
+    else return (tid % L) * G + gi;
+  }
 
   // Loads the rows from row0 on (zeros past the buffer's end), rotates them
   // if asked; returns this thread's largest magnitude.
@@ -93,38 +121,51 @@ struct BlockQuant {
                                         const float* __restrict__ signs, int tid) {
     float amax = 0.f;
 #pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      const int cid = k * 256 + tid;
-      const int row = cid / CPR, ch = cid % CPR;
-      const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-          rx, (unsigned)((row0 + row) * D + ch * 8) * 2u, 0, 0);
-      const u16* e = (const u16*)&w;
+    for (int r = 0; r < RPT; ++r) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[k][j] = __uint_as_float((unsigned)e[j] << 16);
+      for (int gi = 0; gi < G; ++gi) {
+        const int row = row_of(r, tid), ch = chunk_of(r, gi, tid);
+        const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+            rx, (unsigned)((row0 + row) * D + ch * 8) * 2u, 0, 0);
+        const u16* e = (const u16*)&w;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[r * G + gi][j] = __uint_as_float((unsigned)e[j] << 16);
+      }
       if constexpr (ROTATE) {
+        float* y = &x[r * G][0];  // the thread's 8G consecutive columns of this row
+        const int c0 = chunk_of(r, 0, tid) * 8;
+        // stride 1 with the signs folded in: (s0 x0) +- (s1 x1), the
+        // products exact, one rounding each, as sign-then-butterfly gives
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[k][j] *= signs[ch * 8 + j];
-        // strides 1, 2, 4 inside the chunk
+        for (int j = 0; j < 8 * G; j += 2) {
+          const float t = signs[c0 + j + 1] * y[j + 1];
+          const float a = y[j];
+          y[j] = fmaf(signs[c0 + j], a, t);
+          y[j + 1] = fmaf(signs[c0 + j], a, -t);
+        }
+        // strides 2 .. 4G in registers
 #pragma unroll
-        for (int s = 1; s < 8; s <<= 1)
+        for (int st = 2; st < 8 * G; st <<= 1)
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if ((j & s) == 0) {
-              const float a = x[k][j], b = x[k][j + s];
-              x[k][j] = a + b;
-              x[k][j + s] = a - b;
+          for (int j = 0; j < 8 * G; ++j)
+            if ((j & st) == 0) {
+              const float a = y[j], b = y[j + st];
+              y[j] = a + b;
+              y[j + st] = a - b;
             }
-        // strides 8 .. D/2 across the lanes holding one row: the lane with
-        // the bit m clear keeps x + other, the one with it set other - x.
+        // strides >= 8G across the lanes holding the row: the lane with the
+        // bit m clear keeps x + other, the one with it set other - x.
 #pragma unroll
-        for (int m = 1; m < CPR; m <<= 1) {
+        for (int m = 1; m < L; m <<= 1) {
           const float sgn = (tid & m) ? -1.f : 1.f;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[k][j] = fmaf(sgn, x[k][j], lane_xor(x[k][j], m));
+          for (int j = 0; j < 8 * G; ++j) y[j] = fmaf(sgn, y[j], lane_xor(y[j], m));
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[k][j]));
+      for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[r * G + gi][j]));
     }
     return amax;
   }
@@ -134,18 +175,20 @@ struct BlockQuant {
   template <class Sink>
   __device__ __forceinline__ void emit(float inv_s, int tid, Sink sink) const {
 #pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      const int cid = k * 256 + tid;
-      float t[8];
+    for (int r = 0; r < RPT; ++r)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t[j] = fminf(fmaxf(x[k][j] * inv_s, -kE4m3Max), kE4m3Max);
-      int lo = cvt_pk_fp8<false>(t[0], t[1], 0);
-      lo = cvt_pk_fp8<true>(t[2], t[3], lo);
-      int hi = cvt_pk_fp8<false>(t[4], t[5], 0);
-      hi = cvt_pk_fp8<true>(t[6], t[7], hi);
-      const i32x2 packed = {lo, hi};
-      sink(cid / CPR, cid % CPR, packed);
-    }
+      for (int gi = 0; gi < G; ++gi) {
+        const float* xc = x[r * G + gi];
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = fminf(fmaxf(xc[j] * inv_s, -kE4m3Max), kE4m3Max);
+        int lo = cvt_pk_fp8<false>(t[0], t[1], 0);
+        lo = cvt_pk_fp8<true>(t[2], t[3], lo);
+        int hi = cvt_pk_fp8<false>(t[4], t[5], 0);
+        hi = cvt_pk_fp8<true>(t[6], t[7], hi);
+        const i32x2 packed = {lo, hi};
+        sink(row_of(r, tid), chunk_of(r, gi, tid), packed);
+      }
   }
 };
 
@@ -412,7 +455,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     static_assert(BR == kBlock, "a workgroup's queries are one quantisation block");
     __shared__ __attribute__((aligned(16))) char qcodes[kBlock * D];
     __shared__ float red[4];
-    BlockQuant<D, true> bq;
+    BlockQuant<D, true, 4> bq;
     const __amdgpu_buffer_rsrc_t rqb = make_rsrc(Qbf + head * D, (unsigned)N * D * 2u);
     const float s = block_scale(block_max(bq.load(rqb, qt * kBlock, signs, tid), red, tid));
     bq.emit(1.f / s, tid, [&](int row, int ch, i32x2 packed) {
