@@ -64,7 +64,8 @@ __device__ __forceinline__ int cvt_pk_fp8(float a, float b, int old) {
 // 16-lane rows (quad permutes; row rotate by 8); m = 4 through one bit-mode
 // ds_swizzle (two DPP moves before, a half-row mirror then a quad xor 3: the
 // rotating quantisation pass ran 7-9% faster at d = 64 and 128 with the
-// swizzle); wider strides through the LDS crossbar.
+// swizzle); m = 16 through the same swizzle (d = 256); wider strides through
+// the LDS crossbar.
 __device__ __forceinline__ float lane_xor(float v, int m) {
   const int b = __float_as_int(v);
   switch (m) {
@@ -73,6 +74,8 @@ __device__ __forceinline__ float lane_xor(float v, int m) {
     case 4:  // bit-mode swizzle within 32 lanes: and 0x1F, xor 4
       return __int_as_float(__builtin_amdgcn_ds_swizzle(b, (4 << 10) | 0x1F));
     case 8: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, false));
+    case 16:  // bit-mode swizzle within 32 lanes: and 0x1F, xor 16
+      return __int_as_float(__builtin_amdgcn_ds_swizzle(b, (16 << 10) | 0x1F));
     default: return __shfl_xor(v, m);
   }
 }
