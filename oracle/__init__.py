@@ -16,12 +16,12 @@ Contents
                 routine's autograd, closed forms, invariants).
   fp8.py        e4m3fn encode/decode, per-block and per-tensor quantisation
                 with optional random-sign Hadamard rotation (pinned: a library
-                cast, the format's closed forms, H H^T = d I, rotation
-                invariance of attention), and an FP8 attention emulator used
-                only to predict the FP8 kernel's error. The emulator's
-                prediction is "parity unpinned" beyond the reduction case
-                where its inputs are exactly representable (then it equals
-                exact attention up to the rounding of P).
+                cast, the format's closed forms, a hand-built block, H H^T =
+                d I, rotation invariance of attention), and an FP8 attention
+                emulator (P * 2^8 rounded to e4m3) whose error is printed as a
+                prediction next to the kernel's and gates nothing. Its
+                rounding path is "parity unpinned" beyond the reduction to
+                exact attention when P is not rounded.
 """
 from .attention import attention, attention_kv, attention_rows, attention_sampled  # noqa: F401
 from .attention_grad import attention_backward  # noqa: F401

@@ -22,13 +22,14 @@ Readings where the pages are silent (each also listed in the design notes):
     Hadamard matrix. The unnormalised product y = (x * signs) H_d is what is
     quantised (its entries are exact in float64 and, for these inputs,
     usually exact in float32); the 1/sqrt(d) is folded into the stored scale.
-  * the quantisation decision is taken in float32, as the kernel takes it:
-    amax over the block of |float32(y)|, s = float32(amax) / 448 (IEEE float32
-    division; s = 1 for an all-zero block), t = float32(y) * float32(1 / s)
-    (the block's scale applied as a multiplication by its correctly rounded
-    float32 reciprocal), clamped to [-448, 448], rounded to the nearest e4m3
-    value with ties to even. The stored scale is s, or float32(s * float32(1/sqrt(d)))
-    when rotated; dequantised value = e4m3 value * stored scale.
+  * the block scale is s = amax / 448 with amax the largest magnitude of
+    the block's (rotated) values, stored as a float32 (the exact quotient
+    rounded once; s = 1 for an all-zero block, whose codes are all zero);
+    the code of a value y is y / s, clamped to [-448, 448], rounded to the
+    nearest e4m3 value with ties to the even code. y and y / s are taken in
+    float64 (the rotated sums of bf16 inputs are exact there). The stored
+    scale is s, or s / sqrt(d) rounded to float32 when rotated;
+    dequantised value = e4m3 value * stored scale.
 """
 from __future__ import annotations
 
@@ -96,21 +97,18 @@ def quantize(x, per_tensor=False, signs=None, block=BLOCK):
     x = np.asarray(x, dtype=np.float64)
     B, H, N, d = x.shape
     y = rotate_unnormalised(x, signs) if signs is not None else x
-    y32 = y.astype(np.float32)
     nblk = -(-N // block)
-    amax = np.zeros((B, H, nblk), dtype=np.float32)
+    amax = np.zeros((B, H, nblk), dtype=np.float64)
     for t in range(nblk):
-        amax[:, :, t] = np.abs(y32[:, :, t * block:(t + 1) * block, :]).max(axis=(2, 3))
+        amax[:, :, t] = np.abs(y[:, :, t * block:(t + 1) * block, :]).max(axis=(2, 3))
     if per_tensor:
         amax[...] = amax.max()
-    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    inv = (np.float32(1.0) / s).astype(np.float32)                # float32 reciprocal
-    inv_rows = np.repeat(inv, block, axis=2)[:, :, :N, None]      # per row
-    t = (y32 * inv_rows).astype(np.float32)
-    t = np.clip(t, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    s = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)   # stored in float32
+    s_rows = np.repeat(s.astype(np.float64), block, axis=2)[:, :, :N, None]
+    t = np.clip(y / s_rows, -E4M3_MAX, E4M3_MAX)
     codes = e4m3_encode(t)
     if signs is not None:
-        stored = (s * np.float32(1.0 / np.sqrt(d))).astype(np.float32)
+        stored = (s.astype(np.float64) / np.sqrt(d)).astype(np.float32)
     else:
         stored = s
     return codes, stored
@@ -124,25 +122,23 @@ def dequantize(codes, scales, block=BLOCK):
 
 
 def fp8_attention_emulate(q_codes, k_codes, v_codes, sq, sk, sv, causal, scale,
-                          p_scale=256.0, block=BLOCK, round_p=True, v_fold=True):
+                          p_scale=256.0, block=BLOCK, round_p=True):
     """Attention on dequantised FP8 operands with P rounded to e4m3.
 
-    A prediction of the FP8 kernel's error, not a definition of the method:
-    S = scale * Qd Kd^T from the dequantised (and, if rotated, rotated) Q, K;
-    P = exp(S - rowmax); the product P V is taken in e4m3 (QbitAI article,
-    FP8 section), so P is rounded to e4m3 after multiplying by p_scale and,
-    with v_fold, by r_j = (V scale of key j's block) / (largest V block scale
-    of the (batch, head)): the kernel applies V's block scales to P rather
-    than to its accumulator. The row sum is taken over the same rounded
-    values divided by p_scale * r_j, i.e. over the probabilities the product
-    used; O = sum_j Pq_j Vd_j / sum_j Pq_j. Without rounding (round_p=False)
-    this is exact attention on the dequantised operands whatever the scales.
+    A prediction of the FP8 kernel's error, not a definition of the method
+    and not a gate: S = scale * Qd Kd^T from the dequantised (and, if
+    rotated, rotated) Q, K; P = exp(S - rowmax); the product P V is taken in
+    e4m3 (QbitAI article, FP8 section), so P is multiplied by p_scale (to
+    keep small probabilities out of e4m3's subnormal range) and rounded to
+    e4m3; the row sum is taken over the same rounded values, i.e. over the
+    probabilities the product used: O = sum_j Pq_j Vd_j / sum_j Pq_j.
+    Without rounding (round_p=False) this is exact attention on the
+    dequantised operands.
     """
     qd = dequantize(q_codes, sq, block)
     kd = dequantize(k_codes, sk, block)
     vd = dequantize(v_codes, sv, block)
     B, H, N, d = qd.shape
-    sv64 = np.asarray(sv, dtype=np.float64)
     o = np.empty_like(vd)
     for b in range(B):
         for h in range(H):
@@ -152,12 +148,7 @@ def fp8_attention_emulate(q_codes, k_codes, v_codes, sq, sk, sv, causal, scale,
             m = s.max(axis=1, keepdims=True)
             p = np.exp(s - m)
             if round_p:
-                if v_fold:
-                    r = np.repeat(sv64[b, h] / sv64[b, h].max(), block)[:N][None, :]
-                else:
-                    r = np.ones((1, N))
-                f = p_scale * r
-                pq = e4m3_decode(e4m3_encode(np.minimum(p * f, E4M3_MAX))) / f
+                pq = e4m3_decode(e4m3_encode(np.minimum(p * p_scale, E4M3_MAX))) / p_scale
             else:
                 pq = p
             o[b, h] = (pq @ vd[b, h]) / pq.sum(axis=1, keepdims=True)
