@@ -164,6 +164,14 @@ int fwd_splits_for(int B, int H, int N, int d) {
 
 }  // namespace
 
+namespace fa {
+int debug_flags() {
+  const char* e = std::getenv("FA_DEBUG");
+  if (e == nullptr) return 0;
+  return (int)(std::strtol(e, nullptr, 0) & 3);
+}
+}  // namespace fa
+
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

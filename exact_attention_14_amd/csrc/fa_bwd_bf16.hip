@@ -442,12 +442,16 @@ hipError_t bwd_launch(const void* q, const void* k, const void* v, const void* o
   const int nt = (N + 127) / 128;
   const long long nwg = (long long)nt * B * H;
   if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
-  const int hpx = ((long long)B * H) % 8 == 0 ? (int)(((long long)B * H) / 8) : 0;
+  const int dbg = debug_flags();
+  // Causal: whole heads per XCD, longest tiles first, when the heads split
+  // evenly (not under the reversed debug order).
+  const int hpx = ((long long)B * H) % 8 == 0 && !(dbg & 1) ? (int)(((long long)B * H) / 8) : 0;
+  const int nwg_arg = (int)nwg | (dbg << kDbgShift);
   // dQ first: it also writes the row terms D and -LSE log2(e) that the
   // dK/dV kernel reads (stream order makes them visible to it).
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream,
                      (const u16*)q, (const u16*)k, (const u16*)v, (const u16*)dout, (const u16*)o,
-                     lse, nl, dvec, (u16*)dq, N, nt, (int)nwg, hpx, scale);
+                     lse, nl, dvec, (u16*)dq, N, nt, nwg_arg, hpx, scale);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream,
                      (const u16*)q, (const u16*)k, (const u16*)v, (const u16*)dout,
                      (const float*)nl, (const float*)dvec, (u16*)dk, (u16*)dv, N, nt, (int)nwg,

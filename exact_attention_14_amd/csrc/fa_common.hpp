@@ -153,13 +153,36 @@ __device__ __forceinline__ void store_o_lse_staged(u16* O, float* LSE, size_t he
                                         half == 0 ? (unsigned)(q0w + l32) * 4u : kOutOfRange, 0, 0);
 }
 
+// Debug flags of a launch ride in the top bits of the workgroup-count
+// argument (the forward and backward grids stay below 2^24 workgroups):
+// kDbgReverse runs the workgroups in the reverse order and on other XCDs
+// (the host also drops the per-XCD head grouping), kDbgPoison fills the
+// kernel's LDS with 0xFF bytes (NaN in bf16, fp32 and e4m3) before any tile
+// is copied in. Results must not change: each workgroup's output depends
+// only on its own tile, and no tile may be read before its copy has landed.
+constexpr int kDbgShift = 24;
+constexpr int kDbgReverse = 1;
+constexpr int kDbgPoison = 2;
+__device__ __forceinline__ int dbg_flags(int nwg_arg) { return nwg_arg >> kDbgShift; }
+
+// Fills `bytes` (a multiple of 16) of LDS from `p` with 0xFF, shared over
+// `nthreads` threads; the caller waits for all of them (a barrier) before
+// any copy into that memory is issued.
+__device__ __forceinline__ void poison_lds(char* p, int bytes, int tid, int nthreads) {
+  const i32x4 ff = {-1, -1, -1, -1};
+  for (int o = tid * 16; o < bytes; o += nthreads * 16) *(i32x4*)(p + o) = ff;
+}
+
 // Workgroup id -> (head, query-tile rank). Workgroup ids are dealt to the 8
 // XCDs round-robin. With hpx > 0 (B*H = 8*hpx heads) each XCD owns hpx whole
 // heads and starts its workgroups in rank order across them (rank 0 = the
 // longest causal tile first); otherwise consecutive logical ids, i.e. the
-// tiles of one head, run on one XCD.
+// tiles of one head, run on one XCD. `nwg` may carry debug flags in its top
+// bits (kDbgReverse: logical id nwg - 1 - bid).
 __device__ __forceinline__ void tile_of_workgroup(int bid, int nwg, int ntq, int hpx, int& bh,
                                                   int& rank) {
+  if (dbg_flags(nwg) & kDbgReverse) bid = (nwg & ((1 << kDbgShift) - 1)) - 1 - bid;
+  nwg &= (1 << kDbgShift) - 1;
   if (hpx > 0) {
     const int loc = bid >> 3;
     rank = loc / hpx;

@@ -395,10 +395,16 @@ struct TileCopy8 {
 // products of tile t then overlap the row maxima of tile t+1.
 //   * P * 2^8 comes straight out of exp2 (8 is added to the exponent).
 //   * V's block scales are folded into P instead of the accumulator: with
-//     sv_max the largest V block scale of the head, tile t's P is quantised
-//     as P * 2^8 * r_t, r_t = sv_t / sv_max <= 1 (one more term in the exp2
-//     argument), so the accumulator holds sum P V / sv_max and is rescaled
-//     only when the reference maximum moves.
+//     sv_ref a reference V scale of the wave, tile t's P is quantised as
+//     P * 2^8 * r_t, r_t = sv_t / sv_ref (one more term in the exp2
+//     argument), so the accumulator holds sum P V / sv_ref. sv_ref starts
+//     at the head's largest V block scale and moves to sv_t whenever r_t
+//     leaves [2^-4, 1] (a block larger than the reference, or one so much
+//     smaller that its P * 2^8 * r would sink into e4m3's subnormal range:
+//     an all-zero block, whose scale is 1, or blocks of very different
+//     magnitudes); the fp32 accumulator is then rescaled by the old over
+//     the new reference, which costs no precision. So every tile's P keeps
+//     at least 2^4 * P of headroom above e4m3's normal threshold.
 //   * The row sum is taken by one more e4m3 product per tile,
 //     ones(32 x 64) . P^T, whose every output row is sum_k P*2^8*r_t for the
 //     lane's query; divided by r_t it is the sum of exactly the
@@ -422,6 +428,11 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   using CP = TileCopy8<D, NW>;
   constexpr int BR = 32 * NW;
   constexpr float kLazy = 0.75f;
+  // The V fold ratio r stays in [2^-4, 1]: its reciprocal within
+  // [kVLow, kVHigh] (kVLow allows sv_ref * (1/sv_t) to round below 1 when
+  // the two scales are equal; P * 2^8 * r <= 430 * 1.0001 < 448).
+  constexpr float kVLow = 0.9999f;
+  constexpr float kVHigh = 16.f;
   __shared__ __attribute__((aligned(1024))) char ks0[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char vs0[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char ks1[G::TILEB];
@@ -450,6 +461,14 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   const int q_last = min(N, qt * BR + BR) - 1;
   const int T = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
 
+  if (dbg_flags(nwg) & kDbgPoison) {
+    poison_lds(ks0, G::TILEB, tid, NW * 64);
+    poison_lds(vs0, G::TILEB, tid, NW * 64);
+    poison_lds(ks1, G::TILEB, tid, NW * 64);
+    poison_lds(vs1, G::TILEB, tid, NW * 64);
+    __syncthreads();
+  }
+
   // Prologue: copy K_0, load (or quantise) Q, copy V_0 and K_1.
   const CP cp(wave, lane);
   cp.issue(rk, ks0, 0, wave, true);
@@ -459,6 +478,10 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     static_assert(BR == kBlock, "a workgroup's queries are one quantisation block");
     __shared__ __attribute__((aligned(16))) char qcodes[kBlock * D];
     __shared__ float red[4];
+    if (dbg_flags(nwg) & kDbgPoison) {
+      poison_lds(qcodes, kBlock * D, tid, NW * 64);
+      __syncthreads();
+    }
     BlockQuant<D, true, 4> bq;
     const __amdgpu_buffer_rsrc_t rqb = make_rsrc(Qbf + head * D, (unsigned)N * D * 2u);
     const float s = block_scale(block_max(bq.load(rqb, qt * kBlock, signs, tid), red, tid));
@@ -496,32 +519,35 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   for (int v = 0; v < 16; ++v) zero16[v] = 0.f;
   float l_run = 0.f;        // sum of P * 2^8 over the tiles so far
   float m_ref = -INFINITY;  // reference maximum, log2 units of scale * q.k
-  // Largest V block scale of the head (scales are positive; a non-positive
-  // or missing maximum leaves the fold at ratio 1).
+  // Largest V block scale of the head: the first reference of the V fold
+  // (scales are positive; a non-positive scale is read as this maximum, and
+  // a non-positive maximum as 1: finite output without meaning).
   float sv_max = 0.f;
   for (int b = lane; b < nblk; b += 64) sv_max = fmaxf(sv_max, svh[b]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) sv_max = fmaxf(sv_max, __shfl_xor(sv_max, o));
   if (!(sv_max > 0.f)) sv_max = 1.f;
+  float sv_ref = sv_max;  // the reference V scale of the fold (wave-uniform)
   const float c = scale * kLog2e;
   // Per-block factors of the key tiles, lane b holding block b0 + b: the
-  // score factor c * s_Q * s_K (raw MFMA result -> log2 units), log2 of the
-  // V fold ratio r = s_V / sv_max and 1 / r. A tile reads its block's
-  // factors with readlane, so the key loop has no scalar loads (whose waits
-  // also drain the LDS reads) and no divisions; the table is reloaded every
-  // 64 blocks. s_Q is the same for all of the workgroup's queries (one
-  // quantisation block). Measured +5-9% at d = 64 and 128; at d = 256 (one
-  // wave per SIMD, 460 registers) the table cost 3-9%, so there each tile
-  // computes its factors from the scales directly (the same values).
+  // score factor c * s_Q * s_K (raw MFMA result -> log2 units), the block's
+  // V scale and its reciprocal. A tile reads its block's factors with
+  // readlane, so the key loop has no scalar loads (whose waits also drain
+  // the LDS reads) and no divisions; the table is reloaded every 64 blocks.
+  // s_Q is the same for all of the workgroup's queries (one quantisation
+  // block). Measured +5-9% at d = 64 and 128; at d = 256 (one wave per SIMD,
+  // 460 registers) the table cost 3-9%, so there each tile computes its
+  // factors from the scales directly (the same values).
   constexpr bool kTable = D <= 128;
-  float tab_cs = 0.f, tab_lr = 0.f, tab_ir = 1.f;
+  float tab_cs = 0.f, tab_sv = 1.f, tab_isv = 1.f;
+  auto pos_sv = [&](float sv_b) { return sv_b > 0.f ? sv_b : sv_max; };
   auto load_tab = [&](int b0) {
     const int b = min(b0 + lane, nblk - 1);
     const float sk_b = skh[b];
-    const float sv_b = svh[b];
+    const float sv_b = pos_sv(svh[b]);
     tab_cs = c * sq * sk_b;
-    tab_lr = __log2f(sv_b > 0.f ? sv_b / sv_max : 1.f);
-    tab_ir = sv_b > 0.f ? sv_max / sv_b : 1.f;
+    tab_sv = sv_b;
+    tab_isv = 1.f / sv_b;
   };
   if constexpr (kTable) load_tab(0);
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
@@ -608,28 +634,42 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
       cp.issue(rk, kl, (t + 2) * kBC, wave, t + 2 < T);
       cp.issue(rv, vl, (t + 1) * kBC, wave, t + 1 < T);
     }
-    float cs, log2_r, inv_r;
+    float cs, sv_t, isv_t;
     if constexpr (kTable) {
       cs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_cs), blk & 63));
-      log2_r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_lr), blk & 63));
-      inv_r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_ir), blk & 63));
+      sv_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_sv), blk & 63));
+      isv_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_isv), blk & 63));
     } else {
-      const float sv_b = svh[blk];
       cs = c * sq * skh[blk];
-      log2_r = __log2f(sv_b > 0.f ? sv_b / sv_max : 1.f);
-      inv_r = sv_b > 0.f ? sv_max / sv_b : 1.f;
+      sv_t = pos_sv(svh[blk]);
+      isv_t = 1.f / sv_t;
     }
+    // 1 / r_t = sv_ref / sv_t (IEEE products: the accumulator's scaling and
+    // the row sum use these; the fold factor inside exp2 only needs to be
+    // close, its error cancels between P V and the row sum). The reference
+    // moves when r_t > 1 (beyond rounding) or r_t < 2^-4.
+    float inv_r = sv_ref * isv_t;
+    const bool vmove = inv_r < kVLow || inv_r > kVHigh;
     const float mx = mt * cs;
-    if (__any(mx - m_ref > kLazy)) {
+    if (__any(vmove || mx - m_ref > kLazy)) {
+      // New reference maximum (per lane) and, if the V fold ratio left its
+      // window, new reference V scale sv_t: O and l follow the maximum, O
+      // also the V reference (l counts probabilities, not P * r).
       const float m_new = fmaxf(m_ref, mx);
-      const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m_new);
-      l_run *= alpha;
+      const float am = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m_new);
+      const float alpha = vmove ? am * inv_r : am;
+      l_run *= am;
 #pragma unroll
       for (int i = 0; i < G::NO; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
       m_ref = m_new;
+      if (vmove) {
+        sv_ref = sv_t;
+        inv_r = 1.f;
+      }
     }
+    const float log2_r = inv_r == 1.f ? 0.f : -__log2f(inv_r);
     // exponent offset: 2^8 headroom, the reference maximum and the V fold
     const float mb = 8.f - ((m_ref == -INFINITY) ? 0.f : m_ref) + log2_r;
     // Stage A: scores of tile t+1; softmax of tile t -> P * 2^8 as e4m3.
@@ -713,7 +753,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   __syncthreads();
   char* const slot = wave == 0 ? ks0 : wave == 1 ? ks1 : wave == 2 ? vs0 : vs1;
   const float l_tot = l_run;  // sum of P * 2^8
-  store_o_lse_staged<D>(O, LSE, head, N, q0w, lane, oacc, sv_max / l_tot,
+  store_o_lse_staged<D>(O, LSE, head, N, q0w, lane, oacc, sv_ref / l_tot,
                         (m_ref + __log2f(l_tot) - 8.f) * kLn2, slot);
 }
 
@@ -729,17 +769,21 @@ hipError_t fwd_launch(const void* q8, const void* k8, const void* v8, const floa
   const long long nwg = (long long)ntq * B * H;
   if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
   const int nblk = (N + kBlock - 1) / kBlock;
-  const int hpx = ((long long)B * H) % 8 == 0 ? (int)(((long long)B * H) / 8) : 0;
+  const int dbg = debug_flags();
+  // Causal: whole heads per XCD, longest tiles first, when the heads split
+  // evenly (not under the reversed debug order).
+  const int hpx = ((long long)B * H) % 8 == 0 && !(dbg & 1) ? (int)(((long long)B * H) / 8) : 0;
+  const int nwg_arg = (int)nwg | (dbg << kDbgShift);
   if (q8 == nullptr) {
     const float rsqrt_d = (float)(1.0 / sqrt((double)D));  // as the quantisation pass
     hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW, true>), dim3((unsigned)nwg), dim3(NW * 64),
                        0, stream, nullptr, (const uint8_t*)k8, (const uint8_t*)v8, nullptr, sk,
-                       sv, (u16*)o, lse, N, ntq, (int)nwg, hpx, nblk, scale, (const u16*)qbf,
+                       sv, (u16*)o, lse, N, ntq, nwg_arg, hpx, nblk, scale, (const u16*)qbf,
                        signs, rsqrt_d);
   } else {
     hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW, false>), dim3((unsigned)nwg), dim3(NW * 64),
                        0, stream, (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8, sq,
-                       sk, sv, (u16*)o, lse, N, ntq, (int)nwg, hpx, nblk, scale, nullptr, nullptr,
+                       sk, sv, (u16*)o, lse, N, ntq, nwg_arg, hpx, nblk, scale, nullptr, nullptr,
                        0.f);
   }
   return hipGetLastError();

@@ -85,6 +85,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
   const int q_last = min(N, qt * BR + BR) - 1;
   const int T = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
 
+  if (dbg_flags(nwg) & kDbgPoison) {
+    poison_lds(ks0, G::TILEB, tid, NW * 64);
+    poison_lds(vs0, G::TILEB, tid, NW * 64);
+    poison_lds(ks1, G::TILEB, tid, NW * 64);
+    poison_lds(vs1, G::TILEB, tid, NW * 64);
+    __syncthreads();
+  }
+
   // Prologue, in this order: copy K_0, load Q, copy V_0 and K_1. (The
   // compiler's waits for Q then cover K_0 but not the later copies.)
   const CP cp(wave, lane);
@@ -360,11 +368,14 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   const int ntq = (N + 32 * NW - 1) / (32 * NW);
   const long long nwg = (long long)ntq * B * H;
   if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
-  // Causal: whole heads per XCD, longest tiles first, when the heads split evenly.
-  const int hpx = ((long long)B * H) % 8 == 0 ? (int)(((long long)B * H) / 8) : 0;
+  const int dbg = debug_flags();
+  // Causal: whole heads per XCD, longest tiles first, when the heads split
+  // evenly (not under the reversed debug order).
+  const int hpx = ((long long)B * H) % 8 == 0 && !(dbg & 1) ? (int)(((long long)B * H) / 8) : 0;
+  const int nwg_arg = (int)nwg | (dbg << kDbgShift);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                      stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N, ntq,
-                     (int)nwg, hpx, scale);
+                     nwg_arg, hpx, scale);
   return hipGetLastError();
 }
 

@@ -5,6 +5,12 @@
 
 namespace fa {
 
+// Debug flags of the kernel launches (kDbgReverse | kDbgPoison of the device
+// code), read from the environment variable FA_DEBUG at every call; 0 when
+// it is unset. Forward and backward launchers pass them to their kernels in
+// the top bits of the workgroup count.
+int debug_flags();
+
 // bf16 forward: d in {64, 96, 128, 256}.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            float* lse, int B, int H, int N, int d, bool causal,

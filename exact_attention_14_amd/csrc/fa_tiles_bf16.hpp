@@ -44,9 +44,14 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
   return __builtin_bit_cast(bf16x8, c);
 }
 
-// Byte offset for the chunk slots beyond the data width (d = 96): past any
-// head buffer (head buffers are at most 2 GiB), so copies there return zeros
-// without memory traffic.
+// Byte offset for the chunk slots beyond the data width (d = 96). For heads
+// below 1 GiB (N < 5592406 at d = 96) it lies past the head buffer, so those
+// copies return zeros without memory traffic; for larger heads (up to the
+// 2 GiB that N * d <= 2^30 allows) the pad slots receive real data from
+// inside the head, which is harmless: no read of the kernels touches a pad
+// slot. The offset stays at 1 GiB because it is added to the tile base,
+// which is 2^31 for a tile past the sequence end: 2^31 + 2^30 still fits the
+// 32-bit offset, a 2 GiB pad offset would wrap to the start of the buffer.
 constexpr unsigned kPadOffset = 0x40000000u;
 
 // Per-lane byte offsets (tile row 0) of this wave's share of a tile copy of

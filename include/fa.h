@@ -38,6 +38,11 @@
  *     allocated and freed in stream order (hipMallocFromPoolAsync /
  *     hipFreeAsync on `stream`) and retained for reuse until the process
  *     ends, instead of being released after every call.
+ *   - Debugging aid: the environment variable FA_DEBUG (read at every call;
+ *     bit 0 runs the forward and backward kernels' workgroups in reverse
+ *     order, bit 1 fills the forward kernels' on-chip tile memory with NaN
+ *     bytes before any tile is copied in) leaves every result bit for bit
+ *     unchanged; it exists to show exactly that.
  */
 #ifndef FA_H
 #define FA_H
@@ -116,10 +121,14 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *          rotated to x diag(signs) H_d / sqrt(d), H_d the Sylvester Hadamard
  *          matrix (d a power of two). Rotate Q and K with the same signs,
  *          never V.
- * Quantisation: y = x diag(signs) H_d (float32; y = x without rotation),
- * s = amax|y| / 448 over the block (float32; 1 for an all-zero block),
- * code = round-to-nearest-even e4m3(clamp(y * float32(1/s), +-448)); the stored scale is
- * s, or s * (1/sqrt(d)) with rotation.
+ * Quantisation: y = x diag(signs) H_d (y = x without rotation), s = amax|y|
+ * / 448 over the block (1 for an all-zero block), code = the e4m3 value
+ * nearest to y / s (ties to even, clamped to +-448); the stored scale is s,
+ * or s / sqrt(d) with rotation. The kernel takes y, s and the scaled value
+ * in float32 and applies the scale as a product with its correctly rounded
+ * reciprocal, so a code can differ from that of the exact y / s only where
+ * y / s lies within a few float32 ulps of the midpoint between two e4m3
+ * values (then it is the other of the two).
  * Validation order: null x/x8/scales -> INVALID_ARG; B, H or N < 1 ->
  * INVALID_ARG; d not in {64, 96, 128, 256}, or signs given and d not a power
  * of two -> UNSUPPORTED; the size limits of fa_fwd -> TOO_LARGE; misaligned -> MISALIGNED;
@@ -140,14 +149,16 @@ int fa_quant_fp8(const void* x, void* x8, float* scales,
  *              (positive; a non-positive V scale yields finite but
  *              meaningless rows).
  * o : bf16 [B, H, N, d]; lse : float32 [B, H, N] or NULL; d : 64, 128, 256.
- * The probabilities P of a key tile are multiplied by 256 * r, r = (V scale
- * of the tile's block) / (largest V block scale of the (b, h)) <= 1, and
- * rounded to e4m3 for the P V product; the row sum is the float32
+ * The probabilities P of a key tile are multiplied by 256 * r and rounded
+ * to e4m3 for the P V product, r = (V scale of the tile's block) / (a
+ * reference V scale): the reference starts at the largest V block scale of
+ * the (b, h) and moves to a tile's own scale whenever r would leave
+ * [2^-4, 1] (the float32 accumulator is then rescaled). With V block
+ * scales of any spread, all-zero blocks included, 256 * r * P >= 16 * P,
+ * so every P >= 2^-10 (relative to the row's reference maximum) stays in
+ * e4m3's normal range. The row sum is the float32
  * accumulation of those same rounded values divided by r (taken on the
  * matrix cores), so O is normalised by the weights it was formed with.
- * Where one head's V block scales differ by more than about 2^8, the P of
- * the small-scale blocks fall into e4m3's subnormal range and lose relative
- * precision.
  * Validation order as fa_fwd (null scale arrays -> INVALID_ARG).
  */
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
