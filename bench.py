@@ -5,11 +5,13 @@
                     [--extras-only TEXT]
 
 One step is one fa_fwd call (bf16, non-causal) over the workload
-B=4, H=16, N=2048, d=128 with inputs resident in HBM. The metric is attention
+B=1, H=16, N=16384, d=128 (the longest row of the sequence sweep at 16k
+tokens, hidden 2048) with inputs resident in HBM. The metric is attention
 TFLOP/s = 4*B*H*N^2*d / time (halved for causal masks). Rank 0 prints one JSON
-line. The extra measurements (causal, the sequence and head-dimension sweeps,
-the FP8 path, the backward pass) ride along in "extra"; the CPU baseline times the float64 oracle
-on a bounded sample of the same workload.
+line. The extra measurements (B=4 H=16 N=2048, causal, the sequence and
+head-dimension sweeps, the FP8 path, the backward pass) ride along in "extra";
+"roofline_fp8" is the e4m3 kernel on the FP8 workload; the CPU baseline times
+the float64 oracle on a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -26,9 +28,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2516.6   # TFLOP/s, dense MFMA, MI355X published
 PEAK_FP8 = 5033.2    # TFLOP/s, dense MFMA, MI355X published
-WORKLOAD = dict(B=4, H=16, N=2048, d=128, causal=False)
+WORKLOAD = dict(B=1, H=16, N=16384, d=128, causal=False)
 KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_14_amd", "csrc", "fa_fwd_bf16.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_B4H16N2048d128.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_B1H16N16384d128.json")
+FP8_WORKLOAD = dict(B=2, H=16, N=8192, d=128, causal=False)
 
 
 PEAK_HBM = 8e12      # B/s, MI355X published
@@ -49,12 +52,11 @@ def source_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def time_calls(fn, steps, warmup, min_warm_s=0.3):
-    """Average duration (ms) of fn() over `steps` calls, HIP events on the
-    current stream (the stream the library launches on). The untimed warm-up
-    runs at least `warmup` calls and at least `min_warm_s` seconds: after the
-    idle spell of generating inputs on the host the GPU clock needs some tens
-    of milliseconds to ramp back up."""
+def settle(fn, warmup, min_warm_s=0.3):
+    """Runs fn() at least `warmup` times and for at least `min_warm_s`
+    seconds (synchronising every 16 calls); returns the seconds spent. After
+    the idle spell of generating inputs on the host the GPU clock needs some
+    tens of milliseconds of load to ramp back up."""
     import torch
     t0 = time.perf_counter()
     n = 0
@@ -64,6 +66,17 @@ def time_calls(fn, steps, warmup, min_warm_s=0.3):
         if n % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_calls(fn, steps, warmup, min_warm_s=0.3):
+    """Average duration (ms) of fn() over `steps` calls, HIP events on the
+    current stream (the stream the library launches on). The untimed warm-up
+    runs at least `warmup` calls and at least `min_warm_s` seconds: after the
+    idle spell of generating inputs on the host the GPU clock needs some tens
+    of milliseconds to ramp back up."""
+    import torch
+    settle(fn, warmup, min_warm_s)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(steps):
@@ -163,6 +176,7 @@ def extras(fa, only=None):
         run_bwd("backward head-dim sweep (fa_bwd)", 2, 16, 8192, d, True,
                 fa_inputs.SEEDS["dim_sweep_base"] + i, steps=20)
 
+    run("mid non-causal", 4, 16, 2048, 128, False, fa_inputs.SEEDS["mid"])
     run("mid causal", 4, 16, 2048, 128, True, fa_inputs.SEEDS["mid"])
     for N in (512, 1024, 2048, 4096, 8192, 16384):
         seed = fa_inputs.SEEDS["seq_sweep_base"] + int(math.log2(N // 512))
@@ -171,11 +185,19 @@ def extras(fa, only=None):
     for i, d in enumerate((64, 96, 128, 256)):
         run("head-dim sweep", 2, 16, 8192, d, True, fa_inputs.SEEDS["dim_sweep_base"] + i)
 
-    # FP8: B=2 H=16 N=8192 d=128 non-causal, outliers replacing 0.1% of entries,
-    # 128-row block scales with the random-sign Hadamard rotation of Q and K.
-    if not want("fp8"):
-        return out
-    B, H, N, d = 2, 16, 8192, 128
+    return out
+
+
+def fp8_measurements(fa, only=None, steps=200):
+    """The FP8 workload (B=2 H=16 N=8192 d=128 non-causal, outliers replacing
+    0.1% of entries, 128-row block scales with the random-sign Hadamard
+    rotation of Q and K): the e4m3 kernel alone (its roofline object against
+    the fp8 peak), the end-to-end path, the quantiser. Returns
+    (roofline_fp8, extra entries)."""
+    import torch
+    import fa_inputs
+    out = []
+    B, H, N, d = (FP8_WORKLOAD[x] for x in ("B", "H", "N", "d"))
     g = fa_inputs.make_qkv(B, H, N, d, fa_inputs.SEEDS["fp8"], "outlier_replace")
     q, k, v = (fa_inputs.to_torch_bf16(x, "cuda") for x in (g.q_bits, g.k_bits, g.v_bits))
     signs = torch.from_numpy(fa_inputs.random_signs(d, fa_inputs.SEEDS["fp8_signs"])).cuda()
@@ -185,29 +207,49 @@ def extras(fa, only=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     f = flops(B, H, N, d, False)
-    ms = time_calls(lambda: fa.fwd_fp8(q8, k8, v8, sq, sk, sv, out=o, lse=lse), 100, 3)
+    ms = time_calls(lambda: fa.fwd_fp8(q8, k8, v8, sq, sk, sv, out=o, lse=lse), steps, 3)
+    achieved = f / (ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8, 4), "traffic": None,
+            "kernel": "fwd_fp8_kernel<128,false,4,false>", "kernel_ms": round(ms, 5),
+            "workload": f"fa_fwd_fp8 B={B} H={H} N={N} d={d} e4m3 non-causal, block scales + "
+                        "Hadamard, outliers replacing 0.1% of entries",
+            "x_bf16_same_shape": None}
     out.append({"name": "fp8 kernel (fa_fwd_fp8)", "B": B, "H": H, "N": N, "d": d,
                 "causal": False, "dtype": "fp8_e4m3", "ms": round(ms, 4),
-                "tflops": round(f / (ms * 1e-3) / 1e12, 1),
-                "pct_peak": round(100 * f / (ms * 1e-3) / 1e12 / PEAK_FP8, 1)})
-    ms = time_calls(lambda: fa.fwd(q, k, v, dtype=fa.FA_FP8_E4M3, out=o, lse=lse), 100, 3)
-    out.append({"name": "fp8 end to end (fa_fwd, quantisation included)", "B": B, "H": H,
-                "N": N, "d": d, "causal": False, "dtype": "fp8_e4m3", "ms": round(ms, 4),
-                "tflops": round(f / (ms * 1e-3) / 1e12, 1),
-                "pct_peak": round(100 * f / (ms * 1e-3) / 1e12 / PEAK_FP8, 1)})
-    ms = time_calls(lambda: fa.quant_fp8(q, signs=signs, out=q8, scales=sq), 100, 3)
-    nbytes = B * H * N * d * 3 + B * H * ((N + 127) // 128) * 4
-    out.append({"name": "fp8 quantiser with rotation (fa_quant_fp8, one tensor)", "B": B, "H": H,
-                "N": N, "d": d, "ms": round(ms, 4),
-                "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 8e12, 1)})
-    return out
+                "tflops": round(achieved, 1), "pct_peak": round(100 * achieved / PEAK_FP8, 1)})
+    # the bf16 kernel on the same shape, for the FP8/bf16 ratio
+    ms_bf = time_calls(lambda: fa.fwd(q, k, v, out=o, lse=lse), steps, 3)
+    roof["x_bf16_same_shape"] = round(ms_bf / ms, 3)
+    if only is None or "fp8" in only:
+        ms = time_calls(lambda: fa.fwd(q, k, v, dtype=fa.FA_FP8_E4M3, out=o, lse=lse), 100, 3)
+        out.append({"name": "fp8 end to end (fa_fwd, quantisation included)", "B": B, "H": H,
+                    "N": N, "d": d, "causal": False, "dtype": "fp8_e4m3", "ms": round(ms, 4),
+                    "tflops": round(f / (ms * 1e-3) / 1e12, 1),
+                    "pct_peak": round(100 * f / (ms * 1e-3) / 1e12 / PEAK_FP8, 1)})
+        ms = time_calls(lambda: fa.quant_fp8(q, signs=signs, out=q8, scales=sq), 100, 3)
+        nbytes = B * H * N * d * 3 + B * H * ((N + 127) // 128) * 4
+        out.append({"name": "fp8 quantiser with rotation (fa_quant_fp8, one tensor)", "B": B,
+                    "H": H, "N": N, "d": d, "ms": round(ms, 4),
+                    "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 8e12, 1)})
+    del q, k, v, q8, k8, v8, o, lse
+    return roof, out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(budget_s=12.0):
-    """Times the float64 oracle on whole heads of the bench workload until
+    """Times the float64 oracle on whole heads of the headline workload until
     about `budget_s` seconds of CPU work have run."""
-    import numpy as np
     import fa_inputs
     from oracle import attention
     try:
@@ -216,20 +258,21 @@ def cpu_baseline(budget_s=12.0):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     B, H, N, d = WORKLOAD["B"], WORKLOAD["H"], WORKLOAD["N"], WORKLOAD["d"]
-    g = fa_inputs.make_qkv(B, H, N, d, fa_inputs.SEEDS["mid"])
+    g = fa_inputs.make_qkv(1, 2, N, d, fa_inputs.SEEDS["seq_sweep_base"] + 5)
     q, k, v = g.q, g.k, g.v
     heads = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
-        b, h = divmod(heads % (B * H), H)
-        attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
-                  WORKLOAD["causal"])
+        h = heads % 2
+        attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], WORKLOAD["causal"])
         heads += 1
     dt = time.perf_counter() - t0
     tf = heads * flops(1, 1, N, d, WORKLOAD["causal"]) / dt / 1e12
     return {"value": round(tf, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} (batch, head) slices (cycling over the {B * H} of B=4 H=16 "
-                      f"N=2048 d=128, non-causal), float64 NumPy, {dt:.1f} s"}
+            "cpu_model": cpu_model(),
+            "sample": f"{heads} (batch, head) slices of N={N} d={d} non-causal (the headline "
+                      f"workload has {B * H}), float64 NumPy with S and P materialised, "
+                      f"{dt:.1f} s"}
 
 
 def traffic_record():
@@ -246,12 +289,16 @@ def traffic_record():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # About 0.3 s each on the default workload: the warm-up covers the clock
-    # ramp after the host-side input generation.
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=2000)
+    # The default run times about 0.4 s of the headline (1.8 ms per step);
+    # the warm-up runs at least this many steps and at least 0.3 s.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 roofline object")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="only the FP8 roofline object (e4m3 kernel on the FP8 workload, "
+                         "--steps timed calls), printed as one JSON line")
     ap.add_argument("--extras-only", default=None, metavar="TEXT",
                     help="run only the extra measurements whose name contains TEXT")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -275,15 +322,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.fp8_only:
+        roof, _ = fp8_measurements(fa, "", steps=args.steps)
+        print(json.dumps({"roofline_fp8": roof}), flush=True)
+        return
+
     B, H, N, d, causal = (WORKLOAD[x] for x in ("B", "H", "N", "d", "causal"))
-    q, k, v = device_qkv(B, H, N, d, fa_inputs.SEEDS["mid"])
+    q, k, v = device_qkv(B, H, N, d, fa_inputs.SEEDS["seq_sweep_base"] + 5)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     step = lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # untimed: at least --warmup steps and at least 0.3 s (clock settling)
+    warm_s = settle(step, args.warmup)
+    # timed: exactly --steps steps, bracketed by synchronisations; the events
+    # sit on torch's current stream, which is the stream the library launches on
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
@@ -303,24 +357,30 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "attention fwd B=4 H=16 N=2048 d=128 bf16 non-causal",
+        "config": {"workload": f"attention fwd B={B} H={H} N={N} d={d} bf16 non-causal "
+                               "(sequence sweep at 16k tokens, hidden 2048)",
                    "global_batch": B, "seq_len": N, "heads": H, "head_dim": d,
                    "causal": causal, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
-                     "traffic": traffic_record(), "kernel": "fwd_bf16_kernel<128,false>",
+                     "traffic": traffic_record(), "kernel": "fwd_bf16_kernel<128,false,4>",
                      "kernel_ms": round(kernel_ms, 5)},
     }
     del q, k, v, o, lse
+    fp8_extra = []
+    if not args.no_fp8:
+        rec["roofline_fp8"], fp8_extra = fp8_measurements(
+            fa, "" if args.no_extras else args.extras_only)
     if not args.no_extras:
-        rec["extra"] = extras(fa, args.extras_only)
+        rec["extra"] = extras(fa, args.extras_only) + fp8_extra
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline()
     print(json.dumps(rec), flush=True)
