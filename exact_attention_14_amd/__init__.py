@@ -26,9 +26,11 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_MISALIGNED = -3
 FA_ERR_HIP = -4
 FA_ERR_TOO_LARGE = -5
+FA_ERR_SCRATCH_LIMIT = -6
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
-EXPORTS = ("fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_bwd", "fa_fwd_splitkv", "fa_splitkv_splits",
-           "fa_status_string", "fa_version")
+EXPORTS = ("fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_bwd", "fa_fwd_splitkv",
+           "fa_fwd_splitkv_noalloc", "fa_splitkv_splits", "fa_status_string", "fa_version")
 
 
 class FAError(RuntimeError):
@@ -60,6 +62,8 @@ def _load():
     lib.fa_bwd.restype = i
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = i
     lib.fa_splitkv_splits.argtypes = [i, i, i, i, i]
     lib.fa_splitkv_splits.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -216,6 +220,36 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     _launch(lib.fa_fwd_splitkv, "fa_fwd_splitkv", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
             _ptr(lse), B, H, Nq, Nk, d, int(bool(causal)), float(scale), int(num_splits))
+    return o, lse
+
+
+def fwd_splitkv_noalloc(q, k, v, causal: bool = False, scale: float | None = None,
+                        num_splits: int = 0, out=None, lse=None, return_lse: bool = True):
+    """fwd_splitkv through the allocation-free entry point: the library's
+    part of the call allocates nothing (its scratch is a fixed array of
+    NOALLOC_SCRATCH_BYTES per device, shared by all such calls on it).
+    Pass `out` (and `lse`, or return_lse=False) to allocate nothing here
+    either, e.g. under graph capture."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 [B, H, N, d] tensor")
+        if t.device.type != "cuda" or t.device != q.device:
+            raise ValueError(f"{name} must be on q's GPU")
+    B, H, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError(f"k, v must be [B, H, Nk, d] matching q: {tuple(k.shape)} {tuple(v.shape)}")
+    Nk = k.shape[2]
+    _check_buf(out, "out", q.shape, torch.bfloat16, q.device)
+    _check_buf(lse, "lse", (B, H, Nq), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _launch(lib.fa_fwd_splitkv_noalloc, "fa_fwd_splitkv_noalloc", q.device, _ptr(q), _ptr(k),
+            _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, int(bool(causal)), float(scale),
+            int(num_splits))
     return o, lse
 
 

@@ -267,9 +267,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   return hip_status(ef, "hipFreeAsync");
 }
 
-int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                   int H, int Nq, int Nk, int d, int causal, float scale, int num_splits,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+// fa_fwd_splitkv's checks in the header's order up to the size limits;
+// *splits receives the normalised split count.
+int splitkv_check(const void* q, const void* k, const void* v, void* o, int B, int H, int Nq,
+                  int Nk, int d, int causal, float scale, int num_splits, int* splits) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && Nq > Nk) return FA_ERR_INVALID_ARG;
@@ -278,16 +283,59 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   if ((long long)Nk * d > (1LL << 30) || (long long)Nq * d > (1LL << 29) ||
       (long long)B * H >= (1LL << 31))
     return FA_ERR_TOO_LARGE;
-  const int splits = fa::split_count(B, H, Nq, Nk, num_splits);
-  if (fa::split_work_items(B, H, Nq, d, splits) > kMaxWorkItems) return FA_ERR_TOO_LARGE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      (lse != nullptr && !aligned16(lse)))
-    return FA_ERR_MISALIGNED;
+  *splits = fa::split_count(B, H, Nq, Nk, num_splits);
+  if (fa::split_work_items(B, H, Nq, d, *splits) > kMaxWorkItems) return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+bool splitkv_aligned(const void* q, const void* k, const void* v, void* o, float* lse) {
+  return aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) &&
+         (lse == nullptr || aligned16(lse));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int Nq, int Nk, int d, int causal, float scale, int num_splits,
+                   void* stream) {
+  int splits = 0;
+  const int st = splitkv_check(q, k, v, o, B, H, Nq, Nk, d, causal, scale, num_splits, &splits);
+  if (st != FA_OK) return st;
+  if (!splitkv_aligned(q, k, v, o, lse)) return FA_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (log_enabled())
     std::fprintf(stderr, "[fa] fa_fwd_splitkv B=%d H=%d Nq=%d Nk=%d d=%d causal=%d splits=%d\n", B,
                  H, Nq, Nk, d, causal, splits);
   return run_split_path(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, splits, s);
+}
+
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                           int num_splits, void* stream) {
+  int splits = 0;
+  const int st = splitkv_check(q, k, v, o, B, H, Nq, Nk, d, causal, scale, num_splits, &splits);
+  if (st != FA_OK) return st;
+  const unsigned long long need =
+      (unsigned long long)splits * B * H * Nq * (d + 1) * sizeof(float);
+  if (need > FA_NOALLOC_SCRATCH_BYTES) {
+    if (log_enabled())
+      std::fprintf(stderr, "[fa] fa_fwd_splitkv_noalloc needs %llu bytes of scratch, holds %u\n",
+                   need, (unsigned)FA_NOALLOC_SCRATCH_BYTES);
+    return FA_ERR_SCRATCH_LIMIT;
+  }
+  if (!splitkv_aligned(q, k, v, o, lse)) return FA_ERR_MISALIGNED;
+  float* ws = nullptr;
+  hipError_t e = fa::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "scratch address");
+  if (log_enabled())
+    std::fprintf(stderr,
+                 "[fa] fa_fwd_splitkv_noalloc B=%d H=%d Nq=%d Nk=%d d=%d causal=%d splits=%d\n",
+                 B, H, Nq, Nk, d, causal, splits);
+  return hip_status(fa::launch_fwd_split_bf16(q, k, v, o, lse, ws, B, H, Nq, Nk, d, causal != 0,
+                                              splits, scale, static_cast<hipStream_t>(stream)),
+                    "fwd_split launch");
 }
 
 int fa_splitkv_splits(int B, int H, int Nq, int Nk, int num_splits) {
@@ -303,6 +351,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_TOO_LARGE: return "size beyond 32-bit index limits";
+    case FA_ERR_SCRATCH_LIMIT:
+      return "needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

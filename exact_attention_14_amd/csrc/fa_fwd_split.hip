@@ -17,9 +17,11 @@
 //   LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 
 #include <type_traits>
 
+#include "../../include/fa.h"
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 #include "fa_tiles_bf16.hpp"
@@ -430,6 +432,33 @@ hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, vo
     default:
       return hipErrorInvalidValue;
   }
+}
+
+// Scratch of the allocation-free split-KV entry point (the partial outputs
+// and log-sum-exps of the splits), for callers that cannot allocate device
+// memory. Each device the library runs on holds its own copy until the
+// process ends. In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(float** ws) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    // once per device, with that device current: the address of its copy
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *ws = static_cast<float*>(ptrs[dev]);
+  return hipSuccess;
 }
 
 }  // namespace fa

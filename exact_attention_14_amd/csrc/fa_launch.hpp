@@ -60,4 +60,9 @@ hipError_t launch_quant_kv_fp8(const void* k, const void* v, void* k8, void* v8,
                                float* sv, float* signs, unsigned long long key, int B, int H,
                                int N, int d, hipStream_t stream);
 
+// The device address of this device's copy of the allocation-free entry
+// point's scratch (FA_NOALLOC_SCRATCH_BYTES bytes); looked up once per
+// device, with that device current, then reused. Allocates nothing.
+hipError_t noalloc_scratch(float** ws);
+
 }  // namespace fa

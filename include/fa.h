@@ -32,12 +32,14 @@
  *   - Arguments are validated on the host before any HIP call, in the order
  *     listed for each function. No C++ exception crosses this boundary.
  *     Nothing is printed unless the environment variable FA_LOG=1 is set.
- *   - Thread-safe and re-entrant. The only state the library keeps is one
- *     memory pool per device for stream-ordered scratch (entry points that
- *     need scratch say so): created on first use under a lock, its memory is
+ *   - Thread-safe and re-entrant. The state the library keeps: one memory
+ *     pool per device for stream-ordered scratch (entry points that need
+ *     scratch say so), created on first use under a lock, its memory
  *     allocated and freed in stream order (hipMallocFromPoolAsync /
  *     hipFreeAsync on `stream`) and retained for reuse until the process
- *     ends, instead of being released after every call.
+ *     ends instead of being released after every call; and the fixed scratch
+ *     array of the allocation-free entry point (fa_fwd_splitkv_noalloc),
+ *     which is shared by its calls on a device.
  *   - Debugging aid: the environment variable FA_DEBUG (read at every call;
  *     bit 0 runs the forward and backward kernels' workgroups in reverse
  *     order, bit 1 fills the forward kernels' on-chip tile memory with NaN
@@ -62,8 +64,10 @@ typedef enum fa_status {
     FA_ERR_UNSUPPORTED = -2,   /* head dimension or dtype not instantiated       */
     FA_ERR_MISALIGNED = -3,    /* a tensor pointer is not 16-byte aligned        */
     FA_ERR_HIP = -4,           /* the HIP runtime reported an error at launch    */
-    FA_ERR_TOO_LARGE = -5      /* N*d above 2^30, B*H above the 32-bit range, or
+    FA_ERR_TOO_LARGE = -5,     /* N*d above 2^30, B*H above the 32-bit range, or
                                   a launch grid above 2^32 - 1 work-items     */
+    FA_ERR_SCRATCH_LIMIT = -6  /* the call needs more scratch than the
+                                  allocation-free entry point holds           */
 } fa_status;
 
 /* Rows per FP8 quantisation block: one fp32 scale per 128 consecutive
@@ -232,6 +236,29 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int Nq, int Nk, int d, int causal, float scale,
                    int num_splits, void* stream);
+
+/*
+ * fa_fwd_splitkv_noalloc - fa_fwd_splitkv for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving (decode) loops,
+ * harnesses that forbid allocation. Same arguments, kernels, split count and
+ * result (bit for bit) as fa_fwd_splitkv; it calls no allocator. Its scratch
+ * (the partial outputs and log-sum-exps, splits * B*H*Nq * (d+1) floats) is
+ * a fixed array of FA_NOALLOC_SCRATCH_BYTES bytes in device memory that each
+ * device the library runs on holds until the process ends; its address is
+ * looked up on the first call on a device. The caller still provides q, k,
+ * v, o and lse.
+ * All calls on one device share that device's array: calls that overlap on
+ * one device (different streams or threads, or a captured graph replayed
+ * while another call runs) race and must be serialised by the caller. Every
+ * partial the merge reads is written by the same call, so nothing needs
+ * clearing between calls.
+ * Validation order: as fa_fwd_splitkv, then a scratch need above
+ * FA_NOALLOC_SCRATCH_BYTES -> SCRATCH_LIMIT (before the alignment check).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                           int num_splits, void* stream);
 
 /* The number of splits fa_fwd_splitkv uses for these sizes (num_splits as
  * passed to it); INVALID_ARG for sizes < 1 or num_splits < 0. Host only. */

@@ -16,8 +16,8 @@ def declared_functions():
 
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
-        ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_quant_fp8", "fa_splitkv_splits",
-         "fa_status_string", "fa_version"])
+        ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc",
+         "fa_quant_fp8", "fa_splitkv_splits", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_all_declared(lib):
@@ -29,7 +29,7 @@ def test_library_exports_all_declared(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.version() >= 100
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.status_string(st) and lib.status_string(st) != "unknown status"
     assert lib.status_string(12345) == "unknown status"
 
@@ -128,8 +128,9 @@ def test_bwd_validation_order(lib):
     assert call(scale=-1.0, dq=P + 2) == lib.FA_ERR_INVALID_ARG
 
 
-def test_splitkv_validation_order(lib):
-    f = lib.lib.fa_fwd_splitkv
+@pytest.mark.parametrize("entry", ["fa_fwd_splitkv", "fa_fwd_splitkv_noalloc"])
+def test_splitkv_validation_order(lib, entry):
+    f = getattr(lib.lib, entry)
     args = dict(q=P, k=P, v=P, o=P, lse=None, B=1, H=1, Nq=1, Nk=100, d=128, causal=0, scale=0.1,
                 splits=0)
 
@@ -151,12 +152,46 @@ def test_splitkv_validation_order(lib):
     # decode, one split: 2^26 one-wave workgroups = 2^32 work-items
     assert call(B=1 << 13, H=1 << 13, Nk=64) == lib.FA_ERR_TOO_LARGE
     # just below the limit the size check passes and the next check decides
-    assert call(B=1 << 13, H=(1 << 13) - 1, Nk=64, o=P + 8) == lib.FA_ERR_MISALIGNED
+    # (the allocation-free entry's scratch cannot hold those 2^26 partial rows)
+    assert call(B=1 << 13, H=(1 << 13) - 1, Nk=64, o=P + 8) == (
+        lib.FA_ERR_MISALIGNED if entry == "fa_fwd_splitkv" else lib.FA_ERR_SCRATCH_LIMIT)
     assert call(o=P + 8) == lib.FA_ERR_MISALIGNED
     assert call(lse=P + 4) == lib.FA_ERR_MISALIGNED
     assert call(q=None, d=256) == lib.FA_ERR_INVALID_ARG
     assert call(causal=1, Nq=101, d=256) == lib.FA_ERR_INVALID_ARG
     assert call(d=256, scale=-1.0) == lib.FA_ERR_UNSUPPORTED
+
+
+def test_splitkv_noalloc_scratch_limit(lib):
+    """The allocation-free entry point refuses calls whose partial results
+    (splits * B*H*Nq * (d+1) floats) exceed its fixed scratch array, after
+    the size checks and before the alignment check; fa_fwd_splitkv takes
+    the same sizes (its scratch comes from the pool)."""
+    f = lib.lib.fa_fwd_splitkv_noalloc
+    g = lib.lib.fa_fwd_splitkv
+    limit = lib.NOALLOC_SCRATCH_BYTES
+
+    def need(B, H, Nq, Nk, d, splits):
+        return lib.splitkv_splits(B, H, Nq, Nk, splits) * B * H * Nq * (d + 1) * 4
+
+    # decode B=4 H=16 Nq=1 Nk=16384 d=128 (automatic splits) fits
+    assert need(4, 16, 1, 16384, 128, 0) <= limit
+    assert f(P, P, P, P + 8, None, 4, 16, 1, 16384, 128, 0, 0.1, 0, None) == lib.FA_ERR_MISALIGNED
+    # 2048 queries x 256 heads x 4 splits x 129 floats: 1 GiB > 32 MiB
+    assert need(16, 16, 2048, 8192, 128, 4) > limit
+    assert f(P, P, P, P, None, 16, 16, 2048, 8192, 128, 0, 0.1, 4, None) == lib.FA_ERR_SCRATCH_LIMIT
+    assert f(P, P, P, P + 8, None, 16, 16, 2048, 8192, 128, 0, 0.1, 4, None) == \
+        lib.FA_ERR_SCRATCH_LIMIT
+    assert g(P, P, P, P + 8, None, 16, 16, 2048, 8192, 128, 0, 0.1, 4, None) == lib.FA_ERR_MISALIGNED
+    # the exact boundary: need == limit passes, one more query row does not
+    B, H, d, Nk, sp = 1, 1, 127, 1 << 14, 1
+    rows = limit // (4 * (d + 1))                 # 65536 rows of 128 floats
+    assert need(B, H, rows, Nk, 96, sp) <= limit  # d = 96: (96+1) floats per row
+    assert f(P, P, P, P + 8, None, 1, 1, rows, Nk, 96, 0, 0.1, 1, None) == lib.FA_ERR_MISALIGNED
+    rows97 = limit // (4 * 97) + 1
+    assert f(P, P, P, P, None, 1, 1, rows97, Nk, 96, 0, 0.1, 1, None) == lib.FA_ERR_SCRATCH_LIMIT
+    assert f(P, P, P, P + 8, None, 1, 1, rows97 - 1, Nk, 96, 0, 0.1, 1, None) == \
+        lib.FA_ERR_MISALIGNED
 
 
 def test_splitkv_split_count(lib):
