@@ -32,6 +32,8 @@ WORKLOAD = dict(B=1, H=16, N=16384, d=128, causal=False)
 KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_14_amd", "csrc", "fa_fwd_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_B1H16N16384d128.json")
 FP8_WORKLOAD = dict(B=2, H=16, N=8192, d=128, causal=False)
+FP8_KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_14_amd", "csrc", "fa_fp8.hip")
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_fp8_B2H16N8192d128.json")
 
 
 PEAK_HBM = 8e12      # B/s, MI355X published
@@ -176,6 +178,30 @@ def extras(fa, only=None):
         run_bwd("backward head-dim sweep (fa_bwd)", 2, 16, 8192, d, True,
                 fa_inputs.SEEDS["dim_sweep_base"] + i, steps=20)
 
+    # The practical matrix-core ceiling of this part: a plain library GEMM
+    # (hipBLASLt through torch) under the same power limit, bf16 and e4m3.
+    if want("gemm ceiling"):
+        n = 8192
+        a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        ms = time_calls(lambda: torch.matmul(a, b), 20, 3)
+        out.append({"name": "gemm ceiling bf16 (torch.matmul 8192^3)", "ms": round(ms, 4),
+                    "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1),
+                    "pct_peak": round(100 * 2.0 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_BF16, 1)})
+        try:
+            a8 = a.to(torch.float8_e4m3fn)
+            b8 = b.t().contiguous().to(torch.float8_e4m3fn).t()
+            one = torch.ones((), device="cuda")
+            ms = time_calls(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one,
+                                                     out_dtype=torch.bfloat16), 20, 3)
+            out.append({"name": "gemm ceiling e4m3 (torch._scaled_mm 8192^3)", "ms": round(ms, 4),
+                        "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1),
+                        "pct_peak": round(100 * 2.0 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_FP8, 1)})
+        except Exception as e:  # the fp8 GEMM may be missing from this build of torch
+            out.append({"name": "gemm ceiling e4m3 (torch._scaled_mm 8192^3)",
+                        "error": str(e)[:200]})
+        del a, b
+
     run("mid non-causal", 4, 16, 2048, 128, False, fa_inputs.SEEDS["mid"])
     run("mid causal", 4, 16, 2048, 128, True, fa_inputs.SEEDS["mid"])
     for N in (512, 1024, 2048, 4096, 8192, 16384):
@@ -210,7 +236,8 @@ def fp8_measurements(fa, only=None, steps=200):
     ms = time_calls(lambda: fa.fwd_fp8(q8, k8, v8, sq, sk, sv, out=o, lse=lse), steps, 3)
     achieved = f / (ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP8, 4), "traffic": None,
+            "frac": round(achieved / PEAK_FP8, 4),
+            "traffic": traffic_record(FP8_TRAFFIC_FILE, FP8_KERNEL_SOURCE),
             "kernel": "fwd_fp8_kernel<128,false,4,false>", "kernel_ms": round(ms, 5),
             "workload": f"fa_fwd_fp8 B={B} H={H} N={N} d={d} e4m3 non-causal, block scales + "
                         "Hadamard, outliers replacing 0.1% of entries",
@@ -275,13 +302,13 @@ def cpu_baseline(budget_s=12.0):
                       f"{dt:.1f} s"}
 
 
-def traffic_record():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+def traffic_record(path=TRAFFIC_FILE, source=KERNEL_SOURCE):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
-    rec = json.load(open(TRAFFIC_FILE))
-    if rec.get("source_sha") != source_sha(KERNEL_SOURCE):
+    rec = json.load(open(path))
+    if rec.get("source_sha") != source_sha(source):
         return None
     return rec.get("traffic_bytes")
 

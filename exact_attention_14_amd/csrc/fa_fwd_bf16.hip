@@ -203,6 +203,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
   // wave to fill the gaps, reads both four MFMAs ahead (+2 to +7%).
   constexpr int RA_K = D == 256 ? 4 : 2;
   constexpr int RA_V = D == 256 ? 8 : 6;
+  // Where the copies of V_{t+1} are issued: beside those of K_{t+2} in
+  // stage A (d <= 128), so that they have a whole stage B more to land
+  // before the next step's wait (same-box A/B against spreading them over
+  // stage B: +0.1 to +2.6% at d <= 128, -1.8% at d = 256, which keeps them
+  // in stage B). The stage of V_{t+1} (that of V_{t-1}) is free once every
+  // wave has passed this step's barrier.
+  constexpr bool V_IN_A = D <= 128;
   // KIND: 0 = steady state (tile t+1 needs no mask), 1 = tile t+1 may need
   // masking, 2 = last tile (t = T-1): there is no tile t+1 to score or copy.
   auto step = [&](auto kind_tag, const char* kr, const char* vr, char* kl, char* vl, int t) {
@@ -241,6 +248,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
     // between the two resident workgroups). The NI copies of K_{t+2} are
     // spread over the stage: issued back to back, the copies of all waves of
     // a CU fill the texture unit's queues and stall the issuing waves.
+    // (d <= 128 issues the copies of V_{t+1} here too, see V_IN_A.)
     __builtin_amdgcn_s_setprio(1);
     if constexpr (!LAST) {
 #pragma unroll
@@ -255,8 +263,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
           s_nxt[kb] = mfma32(a, qreg[kk], s_nxt[kb]);
         }
 #pragma unroll
-        for (int ci = kk * CP::NI / G::NK; ci < (kk + 1) * CP::NI / G::NK; ++ci)
+        for (int ci = kk * CP::NI / G::NK; ci < (kk + 1) * CP::NI / G::NK; ++ci) {
           cp.issue_one(ci, rk, kl, (t + 2) * kBC, wave, t + 2 < T);
+          if constexpr (V_IN_A) cp.issue_one(ci, rv, vl, (t + 1) * kBC, wave, t + 1 < T);
+        }
       }
     }
     softmax_half(0);
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
     // Nothing moves across: keeps stage B's V fragments out of stage A.
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    // Stage B: P V of tile t, with the copies of V_{t+1} spread over it.
+    // Stage B: P V of tile t (d = 256: with the copies of V_{t+1} spread over it).
     float mt_next = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
           const char* blk = vr + (kb * 32 + a * 16) * G::ROWB;
           oacc[i] = mfma32(tr_pair(blk + voff[i][0], blk + voff[i][1]), p[kb][a], oacc[i]);
           const int slot = (kb * 2 + a) * G::NO + i;
-          if constexpr (!LAST) {
+          if constexpr (!LAST && !V_IN_A) {
 #pragma unroll
             for (int ci = slot * CP::NI / (4 * G::NO); ci < (slot + 1) * CP::NI / (4 * G::NO); ++ci)
               cp.issue_one(ci, rv, vl, (t + 1) * kBC, wave, t + 1 < T);
