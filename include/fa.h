@@ -153,13 +153,13 @@ int fa_quant_fp8(const void* x, void* x8, float* scales,
  *              (positive; a non-positive V scale yields finite but
  *              meaningless rows).
  * o : bf16 [B, H, N, d]; lse : float32 [B, H, N] or NULL; d : 64, 128, 256.
- * The probabilities P of a key tile are multiplied by 256 * r and rounded
+ * The probabilities P of a key tile are multiplied by 64 * r and rounded
  * to e4m3 for the P V product, r = (V scale of the tile's block) / (a
  * reference V scale): the reference starts at the largest V block scale of
  * the (b, h) and moves to a tile's own scale whenever r would leave
  * [2^-4, 1] (the float32 accumulator is then rescaled). With V block
- * scales of any spread, all-zero blocks included, 256 * r * P >= 16 * P,
- * so every P >= 2^-10 (relative to the row's reference maximum) stays in
+ * scales of any spread, all-zero blocks included, 64 * r * P >= 4 * P,
+ * so every P >= 2^-8 (relative to the row's reference maximum) stays in
  * e4m3's normal range. The row sum is the float32
  * accumulation of those same rounded values divided by r (taken on the
  * matrix cores), so O is normalised by the weights it was formed with.

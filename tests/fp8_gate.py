@@ -4,7 +4,7 @@ dequantised operands, derived from the rounding of P to e4m3.
 The kernel forms the scores of the dequantised (rotated) operands exactly up
 to float32 rounding, so apart from float32 effects (relative 1e-6) its output
 differs from exact attention on those operands only by the rounding of the
-probabilities it feeds to the e4m3 P V product: it rounds x = P * 2^8 * r to
+probabilities it feeds to the e4m3 P V product: it rounds x = P * 2^6 * r to
 e4m3, with P = exp(score - m) for a reference maximum m at or below the row's
 true maximum (so P >= the oracle's P, relative to the true maximum, and the
 largest P of a row is >= 1) and r the V fold ratio of the key's block, which
@@ -12,7 +12,7 @@ lies in [max(2^-4, s_V / max s_V), 1] (the reference V scale of a wave never
 exceeds the head's largest V block scale, and the fold keeps r >= 2^-4). Its
 row sum adds the same rounded values. Rounding to nearest e4m3 (3 mantissa
 bits; subnormal spacing 2^-9) moves x by at most max(2^-4 x, 2^-10), so each
-P moves by at most  e_j = max(2^-4 P_j, 2^-18 / r_j).
+P moves by at most  e_j = max(2^-4 P_j, 2^-16 / r_j).
 
 With w_j = P_j / sum P and O = sum_j w_j V_j, the kernel returns
 O~ = sum_j P~_j V_j / sum P~, and because sum_j P_j (V_j - O) = 0,
@@ -36,7 +36,7 @@ import numpy as np
 
 P_REL = 2.0 ** -4        # half an e4m3 ulp, relative to the value (3 mantissa bits)
 X_SUB_ABS = 2.0 ** -10   # half the e4m3 subnormal spacing
-HEADROOM = 2.0 ** 8      # the kernel rounds P * 2^8 * r
+HEADROOM = 2.0 ** 6      # the kernel rounds P * 2^6 * r
 R_MIN = 2.0 ** -4        # the V fold ratio never falls below this
 BLOCK = 128
 
