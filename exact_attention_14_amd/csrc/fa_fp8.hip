@@ -442,6 +442,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   // the two scales are equal; P * 2^6 * r <= 430 * 1.0001 < 448).
   constexpr float kVLow = 0.9999f;
   constexpr float kVHigh = 16.f;
+  constexpr int kDsFirst = 4;  // K fragment reads issued before stage A's first product
   __shared__ __attribute__((aligned(1024))) char ks0[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char vs0[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char ks1[G::TILEB];
@@ -548,7 +549,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   // 460 registers) the table cost 3-9%, so there each tile computes its
   // factors from the scales directly (the same values).
   constexpr bool kTable = D <= 128;
-  float tab_cs = 0.f, tab_sv = 1.f, tab_isv = 1.f;
+  float tab_cs = 0.f, tab_sv = 1.f, tab_isv = 1.f, tab_l2sv = 0.f;
   auto pos_sv = [&](float sv_b) { return sv_b > 0.f ? sv_b : sv_max; };
   auto load_tab = [&](int b0) {
     const int b = min(b0 + lane, nblk - 1);
@@ -557,10 +558,16 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     tab_cs = c * sq * sk_b;
     tab_sv = sv_b;
     tab_isv = 1.f / sv_b;
+    tab_l2sv = __log2f(sv_b);
   };
   if constexpr (kTable) load_tab(0);
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  // Kept in registers at d = 128 (rebuilt before every row-sum product they
+  // cost eight moves per tile; at d = 64, three waves per SIMD, the
+  // registers spill instead, and d = 256 ran 1% slower).
+  if constexpr (D == 128) asm volatile("" : "+v"(ones));
+  float l2_ref = __log2f(sv_ref);  // log2 of the reference V scale
 
   // Loop-invariant per-lane LDS offsets (row swizzles depend on row & 15 only).
   int koff[G::NKS][2];
@@ -643,15 +650,17 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
       cp.issue(rk, kl, (t + 2) * kBC, wave, t + 2 < T);
       cp.issue(rv, vl, (t + 1) * kBC, wave, t + 1 < T);
     }
-    float cs, sv_t, isv_t;
+    float cs, sv_t, isv_t, l2_t;
     if constexpr (kTable) {
       cs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_cs), blk & 63));
       sv_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_sv), blk & 63));
       isv_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_isv), blk & 63));
+      l2_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_l2sv), blk & 63));
     } else {
       cs = c * sq * skh[blk];
       sv_t = pos_sv(svh[blk]);
       isv_t = 1.f / sv_t;
+      l2_t = __log2f(sv_t);
     }
     // 1 / r_t = sv_ref / sv_t (IEEE products: the accumulator's scaling and
     // the row sum use these; the fold factor inside exp2 only needs to be
@@ -675,16 +684,18 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
       m_ref = m_new;
       if (vmove) {
         sv_ref = sv_t;
+        l2_ref = l2_t;
         inv_r = 1.f;
       }
     }
-    const float log2_r = inv_r == 1.f ? 0.f : -__log2f(inv_r);
+    // log2 r_t, from the logs of the two scales: 0 when they are equal.
+    const float log2_r = l2_t - l2_ref;
     // exponent offset: 2^6 headroom, the reference maximum and the V fold
     const float mb = kPExp - ((m_ref == -INFINITY) ? 0.f : m_ref) + log2_r;
     // Stage A: scores of tile t+1; softmax of tile t -> P * 2^6 as e4m3.
     __builtin_amdgcn_s_setprio(1);
     if constexpr (!LAST) scores(kr, s_nxt);
-    int pw[8];  // byte b = kb * 16 + v
+    i32x8 pv;  // byte b = kb * 16 + v
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -695,32 +706,46 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
         // Both halves are written, so the first conversion may start from
         // any register: e[0]'s, which it reads anyway (no zeroing move).
         const int w = cvt_pk_fp8<false>(e[0], e[1], __float_as_int(e[0]));
-        pw[kb * 4 + v4] = cvt_pk_fp8<true>(e[2], e[3], w);
+        pv[kb * 4 + v4] = cvt_pk_fp8<true>(e[2], e[3], w);
       }
-    if constexpr (!LAST) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+    // d <= 128: V_t's fragments for stage B are read during stage A, behind
+    // the K reads, so that the P V products do not wait on the LDS (+1 to
+    // +2%); at d = 256 (one wave per SIMD) they are read in stage B (-1%
+    // otherwise).
+    auto read_v = [&](i32x8* vf) {
 #pragma unroll
-      for (int i = 0; i < 2 * G::NKS; ++i) {
+      for (int i = 0; i < G::NO; ++i) {
+        const char* base = vr + voff[i];
+        const i32x2 p0 = tr8(base);
+        const i32x2 p1 = tr8(base + 16 * G::ROWB);
+        const i32x2 p2 = tr8(base + 32 * G::ROWB);
+        const i32x2 p3 = tr8(base + 48 * G::ROWB);
+        vf[i] = (i32x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      }
+    };
+    constexpr bool kVPre = D <= 128;
+    i32x8 vf[G::NO];
+    if constexpr (kVPre) read_v(vf);
+    if constexpr (!LAST) {
+      constexpr int NMF = 2 * G::NKS;             // products of stage A
+      constexpr int DS_K = 2 * NMF, DS_V = kVPre ? 4 * G::NO : 0;
+      constexpr int DS_FIRST = kDsFirst;
+      constexpr int DS_PER = (DS_K + DS_V - DS_FIRST + NMF - 1) / NMF;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, DS_FIRST, 0);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedValu, 10, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, DS_PER, 0);
       }
     }
-    // Nothing moves across: keeps stage B's V fragments out of stage A.
+    // Nothing moves across: the softmax and the reads stay in stage A.
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    const i32x8 pv = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
     // Stage B: P V of tile t and the row sums; then the next tile's row max.
+    if constexpr (!kVPre) read_v(vf);
 #pragma unroll
-    for (int i = 0; i < G::NO; ++i) {
-      const char* base = vr + voff[i];
-      const i32x2 p0 = tr8(base);
-      const i32x2 p1 = tr8(base + 16 * G::ROWB);
-      const i32x2 p2 = tr8(base + 32 * G::ROWB);
-      const i32x2 p3 = tr8(base + 48 * G::ROWB);
-      const i32x8 a = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      oacc[i] = mfma8(a, pv, oacc[i]);
-    }
+    for (int i = 0; i < G::NO; ++i) oacc[i] = mfma8(vf[i], pv, oacc[i]);
     const f32x16 lt = mfma8(ones, pv, zero16);
     l_run = fmaf(lt[0], inv_r, l_run);
     if constexpr (!LAST) {
