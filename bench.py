@@ -155,7 +155,7 @@ def extras(fa, only=None):
         fl = 4.0 * B * H * pairs * d
         nbytes = B * H * (2 * Nk * d * 2 + 2 * Nq * d * 2 + 4 * Nq)
         rec = {"name": name, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": causal,
-               "dtype": "bf16", "splits": fa.splitkv_splits(B, H, Nq, Nk), "ms": round(ms, 4),
+               "dtype": "bf16", "splits": fa.splitkv_splits(B, H, Nq, Nk, causal=causal), "ms": round(ms, 4),
                "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                "pct_peak": round(100 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16, 1),
                "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),

@@ -64,7 +64,7 @@ def _load():
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_splitkv_noalloc.restype = i
-    lib.fa_splitkv_splits.argtypes = [i, i, i, i, i]
+    lib.fa_splitkv_splits.argtypes = [i, i, i, i, i, i]
     lib.fa_splitkv_splits.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -253,9 +253,10 @@ def fwd_splitkv_noalloc(q, k, v, causal: bool = False, scale: float | None = Non
     return o, lse
 
 
-def splitkv_splits(B: int, H: int, Nq: int, Nk: int, num_splits: int = 0) -> int:
+def splitkv_splits(B: int, H: int, Nq: int, Nk: int, num_splits: int = 0,
+                   causal: bool = False) -> int:
     """The number of key splits fa_fwd_splitkv uses for these sizes."""
-    st = lib.fa_splitkv_splits(B, H, Nq, Nk, num_splits)
+    st = lib.fa_splitkv_splits(B, H, Nq, Nk, int(bool(causal)), num_splits)
     if st < 0:
         raise FAError(st, "fa_splitkv_splits")
     return st

@@ -144,20 +144,22 @@ int run_split_path(const void* q, const void* k, const void* v, void* o, float* 
   return hip_status(ef, "hipFreeAsync");
 }
 
-// bf16 self-attention with at most 128 query-tile workgroups (half the
-// compute units) and at least 4096 keys leaves the GPU half idle; the key
-// axis then supplies the parallelism: such calls take the split-KV path (the
-// same products and online softmax, partial results merged by LSE). Measured
-// against the one-pass kernel at d = 128: +8 to +55% at 128 workgroups; from
-// 160 to 240 workgroups the one-pass kernel was faster non-causal (by
-// 20-45%), so those stay on it, as does d = 64 (the one-pass kernel runs
-// three waves per SIMD there: -10% non-causal at 128 workgroups) and d = 96
-// (not measured). Returns the split count to use, or 0 for the one-pass
-// kernel.
-int fwd_splits_for(int B, int H, int N, int d) {
-  if (d != 128 || N < 4096 || (long long)N * d > (1LL << 29)) return 0;
-  if ((long long)B * H * ((N + 127) / 128) > 128) return 0;
-  const int splits = fa::split_count(B, H, N, N, 0);
+// bf16 self-attention with few query-tile workgroups and at least 4096 keys
+// leaves much of the GPU idle; the key axis then supplies the parallelism:
+// such calls take the split-KV path (the forward kernel on key splits,
+// partial results merged by LSE). Same-box timing against the one-pass
+// kernel (TFLOP/s): non-causal at 128 query tiles, d = 128 (B=1 H=2 N=8192)
+// 504 -> 854, d = 96 (B=1 H=4 N=4096) 518 -> 578, d = 64 (B=2 H=2 N=4096)
+// 403 -> 435; causal at 128 tiles d = 96 (B=1 H=2 N=8192) 262 -> 540, at 192
+// tiles (B=1 H=3 N=8192) 452 -> 623, at 224 (B=1 H=7 N=4096) 500 -> 566.
+// Non-causal shapes above 128 tiles stay on the one-pass kernel (B=1 H=3
+// N=8192: 925 against 911 with 2 splits), causal ones above 224 (B=1 H=15
+// N=2048: 484 against 402), and so does d = 256 (no split instance).
+// Returns the split count to use, or 0 for the one-pass kernel.
+int fwd_splits_for(int B, int H, int N, int d, int causal) {
+  if (!split_dim_ok(d) || N < 4096 || (long long)N * d > (1LL << 29)) return 0;
+  if ((long long)B * H * ((N + 127) / 128) > (causal ? 224 : 128)) return 0;
+  const int splits = fa::split_count(B, H, N, N, causal != 0, 0);
   if (splits < 2 || fa::split_work_items(B, H, N, d, splits) > kMaxWorkItems) return 0;
   return splits;
 }
@@ -196,7 +198,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     std::fprintf(stderr, "[fa] fa_fwd dtype=%d B=%d H=%d N=%d d=%d causal=%d scale=%g\n", dtype,
                  B, H, N, d, causal, (double)scale);
   if (dtype == FA_BF16) {
-    const int splits = fwd_splits_for(B, H, N, d);
+    const int splits = fwd_splits_for(B, H, N, d, causal);
     if (splits > 0) return run_split_path(q, k, v, o, lse, B, H, N, N, d, causal, scale, splits, s);
     return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal != 0, scale, s),
                       "fwd_bf16 launch");
@@ -283,7 +285,7 @@ int splitkv_check(const void* q, const void* k, const void* v, void* o, int B, i
   if ((long long)Nk * d > (1LL << 30) || (long long)Nq * d > (1LL << 29) ||
       (long long)B * H >= (1LL << 31))
     return FA_ERR_TOO_LARGE;
-  *splits = fa::split_count(B, H, Nq, Nk, num_splits);
+  *splits = fa::split_count(B, H, Nq, Nk, causal != 0, num_splits);
   if (fa::split_work_items(B, H, Nq, d, *splits) > kMaxWorkItems) return FA_ERR_TOO_LARGE;
   return FA_OK;
 }
@@ -338,9 +340,9 @@ int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
                     "fwd_split launch");
 }
 
-int fa_splitkv_splits(int B, int H, int Nq, int Nk, int num_splits) {
+int fa_splitkv_splits(int B, int H, int Nq, int Nk, int causal, int num_splits) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0) return FA_ERR_INVALID_ARG;
-  return fa::split_count(B, H, Nq, Nk, num_splits);
+  return fa::split_count(B, H, Nq, Nk, causal != 0, num_splits);
 }
 
 const char* fa_status_string(int status) {

@@ -51,10 +51,20 @@ constexpr float kLazyLog2 = 8.f; // rescale threshold, log2 units
 // article: two-stage GEMM-softmax pipelining, S_cur / S_next). K is copied
 // one tile further ahead than V through two-stage LDS rings; the copies are
 // issued as assembly so that only the kernel's own waits order them.
-template <int D, bool CAUSAL, int NW>
+//
+// SPLIT: the key range of each (batch, head, query tile) is cut into `splits`
+// parts of tps 64-key tiles that run as separate workgroups (few heads: the
+// key axis supplies the parallelism). Each writes, in float32, its partial
+// output normalised by its own row sum to Op and its partial log-sum-exp
+// (-inf where it holds no key the query attends) to Lp, slab
+// (batch*H + head)*splits + split of N rows each; a merge by log-sum-exp
+// follows. A workgroup whose split holds no key of its queries writes only
+// the -inf log-sum-exps.
+template <int D, bool CAUSAL, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg, int hpx, float scale) {
+    u16* __restrict__ O, float* __restrict__ LSE, int N, int ntq, int nwg, int hpx, float scale,
+    float* __restrict__ Op, float* __restrict__ Lp, int splits, int tps) {
   using G = Geo<D>;
   using CP = TileCopy<D, NW>;
   constexpr int BR = 32 * NW;
@@ -71,9 +81,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  int bh, qtr;
-  tile_of_workgroup(blockIdx.x, nwg, ntq, CAUSAL ? hpx : 0, bh, qtr);
-  const int qt = CAUSAL ? (ntq - 1 - qtr) : qtr;
+  int bh, qt, sp = 0;
+  if constexpr (SPLIT && CAUSAL) {
+    // Items differ in length (a split past a query tile's diagonal is
+    // empty): longest first, the heads interleaved (workgroup id modulo
+    // B*H, which also keeps each XCD on the same heads when B*H divides 8 or
+    // 8 divides B*H), then query tiles from the last, their splits
+    // consecutive.
+    const int n = nwg & ((1 << kDbgShift) - 1);
+    const int bid = (dbg_flags(nwg) & kDbgReverse) ? n - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int bht = n / (ntq * splits);
+    bh = bid % bht;
+    const int rank = bid / bht;
+    qt = ntq - 1 - rank / splits;
+    sp = rank % splits;
+  } else if constexpr (SPLIT) {
+    int rank;  // a head's items on one XCD, query tiles fastest
+    tile_of_workgroup(blockIdx.x, nwg, ntq * splits, 0, bh, rank);
+    sp = rank / ntq;
+    qt = rank % ntq;
+  } else {
+    int qtr;
+    tile_of_workgroup(blockIdx.x, nwg, ntq, CAUSAL ? hpx : 0, bh, qtr);
+    qt = CAUSAL ? (ntq - 1 - qtr) : qtr;
+  }
   const size_t head = (size_t)bh * (size_t)N;
   const unsigned head_bytes = (unsigned)N * D * 2u;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head * D, head_bytes);
@@ -83,7 +114,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
   const int q0w = qt * BR + wave * 32;
   const int qi = q0w + l32;
   const int q_last = min(N, qt * BR + BR) - 1;
-  const int T = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
+  const int T_all = CAUSAL ? (q_last / kBC + 1) : (N + kBC - 1) / kBC;
+  // Key tiles tb .. tb+T-1 (all of them without SPLIT); below, t counts the
+  // workgroup's own tiles and tile t holds keys (tb + t) * 64 ...
+  const int tb = SPLIT ? sp * tps : 0;
+  const int T = SPLIT ? min(T_all, tb + tps) - tb : T_all;
+  if constexpr (SPLIT) {
+    if (T <= 0) {
+      const size_t slab = ((size_t)bh * splits + sp) * (size_t)N;
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(Lp + slab, (unsigned)N * 4u);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(-INFINITY), rl,
+                                            half == 0 ? (unsigned)qi * 4u : kOutOfRange, 0, 0);
+      return;
+    }
+  }
 
   if (dbg_flags(nwg) & kDbgPoison) {
     poison_lds(ks0, G::TILEB, tid, NW * 64);
@@ -96,7 +140,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
   // Prologue, in this order: copy K_0, load Q, copy V_0 and K_1. (The
   // compiler's waits for Q then cover K_0 but not the later copies.)
   const CP cp(wave, lane);
-  cp.issue(rk, ks0, 0, wave, true);
+  cp.issue(rk, ks0, tb * kBC, wave, true);
   bf16x8 qreg[G::NK];
 #pragma unroll
   for (int kk = 0; kk < G::NK; ++kk) {
@@ -104,8 +148,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
         rq, (unsigned)(qi * D + kk * 16 + half * 8) * 2u, 0, 0);
     qreg[kk] = __builtin_bit_cast(bf16x8, w);
   }
-  cp.issue(rv, vs0, 0, wave, true);
-  cp.issue(rk, ks1, kBC, wave, T > 1);
+  cp.issue(rv, vs0, tb * kBC, wave, true);
+  cp.issue(rk, ks1, (tb + 1) * kBC, wave, T > 1);
 
   f32x16 oacc[G::NO];
 #pragma unroll
@@ -180,7 +224,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(G::NK + 2 * CP::NI));
   __syncthreads();
   scores(ks0, s_cur);
-  mask(s_cur, 0);
+  mask(s_cur, tb * kBC);
   float mt = rowmax(s_cur);
 
   // Tile t: S_t is in s_cur with its row max in mt; K_{t+1} (kr) and V_t (vr)
@@ -264,8 +308,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
         }
 #pragma unroll
         for (int ci = kk * CP::NI / G::NK; ci < (kk + 1) * CP::NI / G::NK; ++ci) {
-          cp.issue_one(ci, rk, kl, (t + 2) * kBC, wave, t + 2 < T);
-          if constexpr (V_IN_A) cp.issue_one(ci, rv, vl, (t + 1) * kBC, wave, t + 1 < T);
+          cp.issue_one(ci, rk, kl, (tb + t + 2) * kBC, wave, t + 2 < T);
+          if constexpr (V_IN_A) cp.issue_one(ci, rv, vl, (tb + t + 1) * kBC, wave, t + 1 < T);
         }
       }
     }
@@ -299,7 +343,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
           if constexpr (!LAST && !V_IN_A) {
 #pragma unroll
             for (int ci = slot * CP::NI / (4 * G::NO); ci < (slot + 1) * CP::NI / (4 * G::NO); ++ci)
-              cp.issue_one(ci, rv, vl, (t + 1) * kBC, wave, t + 1 < T);
+              cp.issue_one(ci, rv, vl, (tb + t + 1) * kBC, wave, t + 1 < T);
           }
         }
       if (kb == 0) {
@@ -308,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
         } else if constexpr (SOFT_A) {
           // Tile t+1's scores are complete: mask them and take their row
           // maximum while the matrix cores work on P V.
-          if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
+          if constexpr (MASK) mask(s_nxt, (tb + t + 1) * kBC);
           mt_next = rowmax(s_nxt);
         } else {
           softmax_half(1);
@@ -326,7 +370,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!SOFT_A && !LAST) {
-      if constexpr (MASK) mask(s_nxt, (t + 1) * kBC);
+      if constexpr (MASK) mask(s_nxt, (tb + t + 1) * kBC);
       mt_next = rowmax(s_nxt);
     }
     if constexpr (!LAST) {
@@ -336,9 +380,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
     }
   };
 
-  // Tiles j < J need no mask for any wave: every key of them precedes the
-  // workgroup's first query (causal) and lies inside the sequence.
-  const int J = CAUSAL ? min(N / kBC, (qt * BR + 1) / kBC) : N / kBC;
+  // Tiles t < J need no mask for any wave: every key of them precedes the
+  // workgroup's first query (causal) and lies inside the sequence (and the
+  // count stops at the workgroup's own tiles).
+  const int Jg = CAUSAL ? min(N / kBC, (qt * BR + 1) / kBC) : N / kBC;
+  const int J = SPLIT ? min(Jg - tb, T) : Jg;
   using Steady = std::integral_constant<int, 0>;
   using Masked = std::integral_constant<int, 1>;
   using Last = std::integral_constant<int, 2>;
@@ -366,9 +412,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
   // its output rows in its own quarter of the two K stages.
   static_assert(NW == 4 && 2 * 32 * 2 * D <= G::TILEB, "staging slots fit the K stages");
   const float l_tot = l_run + xor32(l_run);
-  store_o_lse_staged<D>(O, LSE, head, N, q0w, lane, oacc, 1.f / l_tot,
-                        m_ref * scale + __logf(l_tot),
-                        (wave < 2 ? ks0 : ks1) + (wave & 1) * (32 * 2 * D));
+  if constexpr (SPLIT) {
+    // Partial results, float32: O_s = O / l (0 where the split holds no key
+    // the query attends) and LSE_s = scale*m + ln l (-inf there). Stores
+    // past N fall outside the buffer range and are dropped.
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse = l_tot > 0.f ? m_ref * scale + __logf(l_tot) : -INFINITY;
+    const size_t slab = ((size_t)bh * splits + sp) * (size_t)N;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(Op + slab * D, (unsigned)N * D * 4u);
+#pragma unroll
+    for (int i = 0; i < G::NO; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 w;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) w[x] = oacc[i][4 * g + x] * inv;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, w), ro,
+                                               (unsigned)(qi * D + 32 * i + 8 * g + 4 * half) * 4u,
+                                               0, 0);
+      }
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(Lp + slab, (unsigned)N * 4u);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(lse), rl,
+                                          half == 0 ? (unsigned)qi * 4u : kOutOfRange, 0, 0);
+  } else {
+    store_o_lse_staged<D>(O, LSE, head, N, q0w, lane, oacc, 1.f / l_tot,
+                          m_ref * scale + __logf(l_tot),
+                          (wave < 2 ? ks0 : ks1) + (wave & 1) * (32 * 2 * D));
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -383,9 +453,24 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   // evenly (not under the reversed debug order).
   const int hpx = ((long long)B * H) % 8 == 0 && !(dbg & 1) ? (int)(((long long)B * H) / 8) : 0;
   const int nwg_arg = (int)nwg | (dbg << kDbgShift);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, false>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                      stream, (const u16*)q, (const u16*)k, (const u16*)v, (u16*)o, lse, N, ntq,
-                     nwg_arg, hpx, scale);
+                     nwg_arg, hpx, scale, nullptr, nullptr, 1, 0);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_partials(const void* q, const void* k, const void* v, float* op, float* lp,
+                           int B, int H, int N, int splits, int tps, float scale,
+                           hipStream_t stream) {
+  constexpr int NW = 4;
+  const int ntq = (N + 32 * NW - 1) / (32 * NW);
+  const long long nwg = (long long)ntq * B * H * splits;
+  if (nwg >= (1LL << 31)) return hipErrorInvalidValue;
+  const int nwg_arg = (int)nwg | (debug_flags() << kDbgShift);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, true>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+                     stream, (const u16*)q, (const u16*)k, (const u16*)v, nullptr, nullptr, N, ntq,
+                     nwg_arg, 0, scale, op, lp, splits, tps);
   return hipGetLastError();
 }
 
@@ -403,6 +488,23 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     FA_CASE(96)
     FA_CASE(128)
     FA_CASE(256)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef FA_CASE
+}
+
+hipError_t launch_fwd_bf16_partials(const void* q, const void* k, const void* v, float* op,
+                                    float* lp, int B, int H, int N, int d, bool causal,
+                                    int splits, int tps, float scale, hipStream_t stream) {
+#define FA_CASE(DD)                                                                              \
+  case DD:                                                                                       \
+    return causal ? launch_partials<DD, true>(q, k, v, op, lp, B, H, N, splits, tps, scale, stream) \
+                  : launch_partials<DD, false>(q, k, v, op, lp, B, H, N, splits, tps, scale, stream);
+  switch (d) {
+    FA_CASE(64)
+    FA_CASE(96)
+    FA_CASE(128)
     default:
       return hipErrorInvalidValue;
   }

@@ -57,12 +57,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // The (query tile, split) items of one head run on one accelerator die
-  // (consecutive logical ids), query tiles fastest: they share the split's
-  // key/value tiles in that die's L2.
-  int bh, rank;
-  tile_of_workgroup(blockIdx.x, nwg, nqt * splits, 0, bh, rank);
-  const int sp = rank / nqt, qt = rank % nqt;
+  // Non-causal (and decode): the (query tile, split) items of one head run
+  // on one accelerator die (consecutive logical ids), query tiles fastest:
+  // they share the split's key/value tiles in that die's L2. Causal with
+  // several query tiles: items differ in length (a split past a query tile's
+  // diagonal is empty), so they start longest first: the heads interleaved
+  // (workgroup id modulo B*H, which also keeps each die on the same heads
+  // when B*H divides 8 or 8 divides B*H), then query tiles from the last,
+  // their splits consecutive. Grouping a head's items on one die would give
+  // the die of its last query tiles most of the work.
+  int bh, sp, qt;
+  if constexpr (CAUSAL && NW > 1) {
+    const int bht = nwg / (nqt * splits);
+    bh = (int)(blockIdx.x % (unsigned)bht);
+    const int rank = (int)(blockIdx.x / (unsigned)bht);
+    qt = nqt - 1 - rank / splits;
+    sp = rank % splits;
+  } else {
+    int rank;
+    tile_of_workgroup(blockIdx.x, nwg, nqt * splits, 0, bh, rank);
+    sp = rank / nqt;
+    qt = rank % nqt;
+  }
   const int q0w = qt * BR + wave * 32;
   const int qi = q0w + l32;
   const int delta = Nk - Nq;  // causal: query i attends keys <= i + delta
@@ -72,6 +88,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int t_begin = sp * tps * (kBC / KT);
   int t_end = min(t_all, t_begin + tps * (kBC / KT));
   if (CAUSAL) t_end = min(t_end, (min(Nq, qt * BR + BR) - 1 + delta) / KT + 1);
+  if (t_begin >= t_end) {
+    // None of the workgroup's queries attends a key of this split: only the
+    // -inf log-sum-exps are written; the merge skips such a split without
+    // reading its partial output.
+    const size_t slab = ((size_t)bh * splits + sp) * (size_t)Nq;
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(Lp + slab, (unsigned)Nq * 4u);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(-INFINITY), rl,
+                                          half == 0 ? (unsigned)qi * 4u : kOutOfRange, 0, 0);
+    return;
+  }
 
   const size_t qhead = (size_t)bh * (size_t)Nq;
   const size_t khead = (size_t)bh * (size_t)Nk;
@@ -246,7 +272,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 // Merge of the splits: one thread per (row, 4 output columns), one pass
 // over the splits with a running maximum (the loads of successive splits
-// do not depend on each other, so several are in flight).
+// do not depend on each other, so several are in flight). A split whose
+// log-sum-exp is -inf holds no key the row attends and is skipped: its
+// partial output is zero or, for a wholly empty workgroup, never written.
 template <int D>
 __global__ __launch_bounds__(64) void split_combine_kernel(const float* __restrict__ Op,
                                                            const float* __restrict__ Lp,
@@ -266,6 +294,7 @@ __global__ __launch_bounds__(64) void split_combine_kernel(const float* __restri
 #pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     const float ls = Lp[base + (size_t)s * Nq];
+    if (ls == -INFINITY) continue;  // no attended key in this split (partial output unwritten)
     const f32x4 o = *(const f32x4*)(Op + (base + (size_t)s * Nq) * D + cc * 4);
     const float m_new = fmaxf(m, ls);
     const float f = m == m_new ? 1.f : __expf(m - m_new);  // m = -inf: f = 0
@@ -307,6 +336,7 @@ __global__ __launch_bounds__(kMergeGroups * D / 4) void split_combine_rows_kerne
 #pragma unroll 4
   for (int s = g; s < splits; s += G) {
     const float ls = Lp[base + (size_t)s * Nq];
+    if (ls == -INFINITY) continue;  // no attended key in this split (partial output unwritten)
     const f32x4 o = *(const f32x4*)(Op + (base + (size_t)s * Nq) * D + cc * 4);
     const float m_new = fmaxf(m, ls);
     const float f = m == m_new ? 1.f : __expf(m - m_new);  // m = -inf: f = 0
@@ -353,9 +383,20 @@ hipError_t split_launch(const void* q, const void* k, const void* v, void* o, fl
   const long long rows = (long long)B * H * Nq;
   float* const op = ws;
   float* const lp = ws + rows * splits * D;
-  hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL, NW, KT, S>), dim3((unsigned)nwg), dim3(64 * NW), 0,
-                     stream, (const u16*)q, (const u16*)k, (const u16*)v, op, lp, Nq, Nk, nqt,
-                     splits, tps, (int)nwg, scale);
+  if (NW > 1 && Nq == Nk) {
+    // Self-attention shapes run the one-pass forward kernel on the key
+    // splits (its software pipeline; same-box timing against this file's
+    // split kernel: +17% at B=1 H=2 N=8192 non-causal, +23% at B=1 H=4
+    // N=4096 causal, +13 to +27% at B=1 H=8 N=2048 causal); same partials,
+    // same merge.
+    const hipError_t e = launch_fwd_bf16_partials(q, k, v, op, lp, B, H, Nq, D, CAUSAL, splits,
+                                                  tps, scale, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL, NW, KT, S>), dim3((unsigned)nwg),
+                       dim3(64 * NW), 0, stream, (const u16*)q, (const u16*)k, (const u16*)v, op,
+                       lp, Nq, Nk, nqt, splits, tps, (int)nwg, scale);
+  }
   if (splits >= kMergeGroups) {
     hipLaunchKernelGGL((split_combine_rows_kernel<D>), dim3((unsigned)rows),
                        dim3(kMergeGroups * D / 4), 0, stream, (const float*)op, (const float*)lp,
@@ -387,7 +428,7 @@ hipError_t split_dispatch(const void* q, const void* k, const void* v, void* o, 
 
 }  // namespace
 
-int split_count(int B, int H, int Nq, int Nk, int requested) {
+int split_count(int B, int H, int Nq, int Nk, bool causal, int requested) {
   const int t_all = (Nk + kBC - 1) / kBC;
   long long s = requested;
   if (s <= 0) {
@@ -396,10 +437,18 @@ int split_count(int B, int H, int Nq, int Nk, int requested) {
     if (decode) {
       // two rounds of workgroups (two per compute unit), >= 2 key tiles each
       s = std::min<long long>((1024 + base - 1) / base, std::max(1, t_all / 2));
+    } else if (base >= 256) {
+      s = 1;  // a round of workgroups already
+    } else if (causal) {
+      // causal items differ in length (the longest query tiles set the
+      // makespan): about 768 items, at most 8 splits, >= 4 key tiles each
+      // (measured at 128-224 query tiles: 6 splits at 128, 3-4 at 192-224)
+      s = std::min<long long>(std::min<long long>(8, (768 + base / 2) / base),
+                              std::max(1, t_all / 4));
     } else {
-      // split only below half a round; >= 8 key tiles per split, since every
+      // about 512 items (a round); >= 8 key tiles per split, since every
       // split adds a float32 partial output to write and merge
-      s = base >= 256 ? 1 : std::min<long long>((512 + base - 1) / base, std::max(1, t_all / 8));
+      s = std::min<long long>((512 + base - 1) / base, std::max(1, t_all / 8));
     }
   }
   s = std::max<long long>(1, std::min<long long>(s, t_all));

@@ -39,8 +39,15 @@ hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, vo
                                  float* lse, float* ws, int B, int H, int Nq, int Nk, int d,
                                  bool causal, int splits, float scale, hipStream_t stream);
 
+// The bf16 forward kernel on key splits (Nq = Nk = N, d in {64, 96, 128}):
+// float32 partial outputs `op` and log-sum-exps `lp` of `splits` splits of
+// tps 64-key tiles each, in the layout of launch_fwd_split_bf16's scratch.
+hipError_t launch_fwd_bf16_partials(const void* q, const void* k, const void* v, float* op,
+                                    float* lp, int B, int H, int N, int d, bool causal,
+                                    int splits, int tps, float scale, hipStream_t stream);
+
 // Number of key splits the split-KV forward uses (requested <= 0: automatic).
-int split_count(int B, int H, int Nq, int Nk, int requested);
+int split_count(int B, int H, int Nq, int Nk, bool causal, int requested);
 
 // Work-items (workgroups x threads) of the larger of the split-KV forward's
 // two launches, for the grid-size check.

@@ -216,9 +216,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *   fa_fwd's mask.
  * num_splits : 0 = automatic: for Nq <= 32 (decode) enough splits for two
  *   workgroups per compute unit twice over, at least two 64-key tiles each;
- *   for longer queries a split only when B*H*ceil(Nq/128) < 256, at least
- *   eight tiles each. Else the number of splits (capped at ceil(Nk/64)).
- *   The count used is fa_splitkv_splits().
+ *   for longer queries a split only when B*H*ceil(Nq/128) < 256: about 512
+ *   (query tile, split) items with at least eight tiles each, or, causal,
+ *   about 768 items, at most 8 splits, at least four tiles each. Else the
+ *   number of splits (capped at ceil(Nk/64)). The count used is
+ *   fa_splitkv_splits().
  * Each split's workgroups write a float32 partial output and log-sum-exp to
  * stream-ordered scratch from the library's pool (splits * B*H*Nq * (d+1)
  * floats); a second kernel merges them:
@@ -260,9 +262,10 @@ int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int Nq, int Nk, int d, int causal, float scale,
                            int num_splits, void* stream);
 
-/* The number of splits fa_fwd_splitkv uses for these sizes (num_splits as
- * passed to it); INVALID_ARG for sizes < 1 or num_splits < 0. Host only. */
-int fa_splitkv_splits(int B, int H, int Nq, int Nk, int num_splits);
+/* The number of splits fa_fwd_splitkv uses for these sizes (causal and
+ * num_splits as passed to it); INVALID_ARG for sizes < 1 or num_splits < 0.
+ * Host only. */
+int fa_splitkv_splits(int B, int H, int Nq, int Nk, int causal, int num_splits);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

@@ -196,9 +196,10 @@ def test_splitkv_noalloc_scratch_limit(lib):
 
 def test_splitkv_split_count(lib):
     """Host logic: decode (Nq <= 32) splits into two rounds of workgroups with
-    at least two 64-key tiles each; longer queries split only below half a
-    round, with at least eight tiles per split; never more splits than
-    tiles, and no empty split."""
+    at least two 64-key tiles each; longer queries split only below a round
+    of 256 query-tile workgroups: about 512 items with at least eight tiles
+    per split, or, causal, about 768 items, at most 8 splits, at least four
+    tiles each; never more splits than tiles, and no empty split."""
     s = lib.splitkv_splits
     assert s(1, 1, 1, 1) == 1
     assert s(1, 1, 1, 64 * 10) == 5              # tiles / 2
@@ -211,6 +212,13 @@ def test_splitkv_split_count(lib):
     assert s(1, 2, 200, 200, 0) == 1             # 4 tiles: too few to split
     assert s(1, 4, 4096, 4096) == 4              # 128 workgroups -> 4 splits of 16 tiles
     assert s(4, 16, 2048, 2048) == 1             # 1024 workgroups: no split
+    assert s(1, 4, 4096, 4096, 0, True) == 6     # causal, 128 query tiles: ~768 items
+    assert s(1, 3, 8192, 8192, 0, True) == 4     # 192 query tiles
+    assert s(1, 7, 4096, 4096, 0, True) == 3     # 224 query tiles
+    assert s(1, 1, 2048, 2048, 0, True) == 8     # 16 query tiles: at most 8 splits
+    assert s(1, 1, 512, 512, 0, True) == 2       # 8 key tiles, >= 4 per split
+    assert s(4, 16, 2048, 2048, 0, True) == 1    # a round already
+    assert s(1, 4, 4096, 4096, 5, True) == 5     # requested counts ignore the mask
     with pytest.raises(lib.FAError):
         s(0, 1, 1, 1)
     for B, H, Nq, Nk, req in ((1, 1, 1, 777, 0), (2, 3, 40, 5000, 0), (1, 1, 1, 6400, 33)):

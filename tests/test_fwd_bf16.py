@@ -210,10 +210,11 @@ def test_random_shapes(lib, case):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_few_heads_long_sequence(lib, causal):
-    """At most 128 query-tile workgroups, N >= 4096 and d = 128: fa_fwd takes
-    the split-KV path (key axis split, partials merged by LSE). Full parity
-    with the oracle, and the same bits as fa_fwd_splitkv with automatic
-    splits; the same sizes at d = 64, 96 and 256 keep the one-pass kernel."""
+    """Few query-tile workgroups (at most 128, causal 224) and N >= 4096:
+    fa_fwd takes the split-KV path for d = 64, 96 and 128 (key axis split,
+    partials merged by LSE). Full parity with the oracle, and the same bits
+    as fa_fwd_splitkv with automatic splits; d = 256 keeps the one-pass
+    kernel."""
     import torch
     check_full(lib, 1, 2, 4096, 128, causal, 20000 + causal)
     g = fa_inputs.make_qkv(1, 3, 4096, 128, 20002)

@@ -38,7 +38,7 @@ def run(fa, qb, kb, vb, causal, splits, scale=None):
 
 def check(fa, B, H, Nq, Nk, d, causal, splits, seed, scale=None):
     announce("splitkv", B, H, Nq, Nk, d, "causal" if causal else "noncausal", "splits", splits,
-             "(used", fa.splitkv_splits(B, H, Nq, Nk, splits), ") seed", seed)
+             "(used", fa.splitkv_splits(B, H, Nq, Nk, splits, causal), ") seed", seed)
     qb, kb, vb = make(B, H, Nq, Nk, d, seed)
     o, lse = run(fa, qb, kb, vb, causal, splits, scale)
     o_ref, lse_ref = attention_kv(*(fa_inputs.bf16_bits_to_f64(x) for x in (qb, kb, vb)), causal,
@@ -68,6 +68,12 @@ CASES = [
     # have whole splits without a visible key; 13 splits over 8 merge groups
     (1, 2, 1664, 1664, 64, True, 13),
     (2, 2, 3, 2000, 96, False, 9),
+    # causal with several query tiles and B*H that neither divides 8 nor is
+    # divided by it (longest-first item order over the heads), with empty
+    # workgroups past the diagonal
+    (1, 3, 300, 300, 64, True, 4),
+    (3, 1, 500, 700, 128, True, 6),
+    (1, 5, 1100, 1100, 96, True, 0),
 ]
 
 

@@ -52,7 +52,7 @@ def test_noalloc_matches_pool_entry_two_calls(lib, causal):
     # a larger decode call (64 splits), then a smaller one with fewer splits
     shapes = [(1, 16, 16, 16384, 128, 0), (2, 3, 5, 1000, 64, 3)]
     for i, (B, H, Nq, Nk, d, splits) in enumerate(shapes):
-        used = lib.splitkv_splits(B, H, Nq, Nk, splits)
+        used = lib.splitkv_splits(B, H, Nq, Nk, splits, causal)
         need = used * B * H * Nq * (d + 1) * 4
         announce("noalloc splitkv call", i, B, H, Nq, Nk, d, "causal" if causal else "noncausal",
                  "splits", used, "scratch bytes", need)
