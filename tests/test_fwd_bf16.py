@@ -106,6 +106,35 @@ def test_grid_order_and_lds_poison_bitwise(lib):
             assert torch.equal(l0, l1)
 
 
+def test_split_mode_grid_order_and_lds_poison_bitwise(lib):
+    """The same for the forward kernel's split mode: fa_fwd on few heads (the
+    split-KV route: 4 splits non-causal, 6 causal, items longest first) and
+    fa_fwd_splitkv with 13 splits of 2 key tiles, where many causal
+    workgroups hold no attended key."""
+    import os
+    import torch
+    cases = [("fwd", 1, 2, 4096, 128, None), ("fwd", 1, 3, 4096, 64, None),
+             ("splitkv", 1, 2, 1664, 64, 13)]
+    for (entry, B, H, N, d, splits) in cases:
+        g = fa_inputs.make_qkv(B, H, N, d, 7950 + d)
+        q, k, v = to_device(g)
+        for causal in (False, True):
+            announce("split mode grid order / lds poison", entry, B, H, N, d,
+                     "causal" if causal else "noncausal", "splits", splits)
+            if entry == "fwd":
+                call = lambda: lib.fwd(q, k, v, causal=causal)
+            else:
+                call = lambda: lib.fwd_splitkv(q, k, v, causal=causal, num_splits=splits)
+            o0, l0 = call()
+            os.environ["FA_DEBUG"] = "3"
+            try:
+                o1, l1 = call()
+            finally:
+                del os.environ["FA_DEBUG"]
+            torch.cuda.synchronize()
+            assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+            assert torch.equal(l0, l1)
+
 
 def test_closed_form_identical_keys(lib):
     import torch
