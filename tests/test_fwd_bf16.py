@@ -254,3 +254,7 @@ def test_few_heads_long_sequence(lib, causal):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
     for d in (64, 96, 256):
         check_full(lib, 1, 3, 4096, d, causal, 20002 + d)
+    if causal:
+        # 160 query tiles: causal shapes up to 224 take the split path
+        # (5 splits), non-causal ones the one-pass kernel
+        check_full(lib, 1, 5, 4096, 128, causal, 20003)
