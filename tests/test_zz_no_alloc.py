@@ -49,8 +49,9 @@ def call_c(lib, entry, q, k, v, o, lse, causal, splits):
 @pytest.mark.parametrize("causal", [False, True])
 def test_noalloc_matches_pool_entry_two_calls(lib, causal):
     import torch
-    # a larger decode call (64 splits), then a smaller one with fewer splits
-    shapes = [(1, 16, 16, 16384, 128, 0), (2, 3, 5, 1000, 64, 3)]
+    # a larger decode call (64 splits), then smaller ones with fewer splits:
+    # self-attention (the forward kernel's split mode) and Nq != Nk
+    shapes = [(1, 16, 16, 16384, 128, 0), (1, 2, 640, 640, 128, 4), (2, 3, 5, 1000, 64, 3)]
     for i, (B, H, Nq, Nk, d, splits) in enumerate(shapes):
         used = lib.splitkv_splits(B, H, Nq, Nk, splits, causal)
         need = used * B * H * Nq * (d + 1) * 4
