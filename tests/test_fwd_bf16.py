@@ -52,7 +52,7 @@ def test_mid_config_full(lib, causal):
 
 
 def check_full_pooled(fa, B, H, N, d, causal, seed):
-    """Every element of a BASELINE-size output against the oracle (its heads
+    """Every element of a benchmark-size output against the oracle (its heads
     spread over a thread pool), in the launch configuration the bench
     times."""
     announce("full tensor", B, H, N, d, "causal" if causal else "noncausal", "seed", seed)
