@@ -141,13 +141,16 @@ def test_bwd_past_2_31_elements(lib, big):
             assert ok, (kind, name, st)
 
 
-@pytest.mark.parametrize("Nq,causal", [(1, False), (33, True)])
-def test_splitkv_past_2_31_elements(lib, big, Nq, causal):
+@pytest.mark.parametrize("Nq,causal,splits", [(1, False, 0), (33, True, 0), (N, True, 2)])
+def test_splitkv_past_2_31_elements(lib, big, Nq, causal, splits):
+    """Decode, Nq != Nk, and Nq = Nk with two splits (the forward kernel's
+    split mode; its float32 partials span 17.8 GB)."""
     import torch
     _, k, v, host = big
-    announce("large splitkv", B, H, Nq, N, D, "causal" if causal else "noncausal")
+    announce("large splitkv", B, H, Nq, N, D, "causal" if causal else "noncausal",
+             "splits", splits)
     q = fa_inputs.device_normal_bf16((B, H, Nq, D), fa_inputs.SEEDS["large"] + 4 + Nq)
-    o, lse = lib.fwd_splitkv(q, k, v, causal=causal)
+    o, lse = lib.fwd_splitkv(q, k, v, causal=causal, num_splits=splits)
     torch.cuda.synchronize()
     got, q_h = heads_f64(o), heads_f64(q)
     got_lse = np.stack([lse[b, h].cpu().numpy().astype(np.float64) for b, h in HEADS])
