@@ -81,13 +81,14 @@ typedef enum fa_status {
  * lse     : float32 [B, H, N] or NULL         scale : softmax scale, finite > 0
  *           (callers normally pass 1/sqrt(d), the equation's scaling)
  * d       : 64, 96, 128 or 256 for FA_BF16; 64, 128 or 256 for FA_FP8_E4M3
- * dtype   : FA_BF16 runs the bf16 matrix-core path. With at most 128
- *           query tiles in all (B*H*ceil(N/128) <= 128), N >= 4096 and
- *           d = 128 it runs the split-KV path of fa_fwd_splitkv (automatic
- *           split count; stream-ordered scratch from the library's pool):
- *           the same products and softmax, partial results merged by LSE,
- *           so the output differs from the one-pass kernel's only by
- *           rounding order.
+ * dtype   : FA_BF16 runs the bf16 matrix-core path. With few query tiles
+ *           in all (B*H*ceil(N/128) <= 128, causal <= 224), N >= 4096,
+ *           N*d <= 2^29, d in {64, 96, 128} and an automatic split count
+ *           (fa_splitkv_splits) of at least 2, it runs the split-KV path of
+ *           fa_fwd_splitkv instead (stream-ordered scratch from the
+ *           library's pool): the same products and softmax over key ranges,
+ *           partial results merged by LSE, so the output differs from the
+ *           one-pass kernel's only by rounding order.
  *           FA_FP8_E4M3 runs the FP8 path end to end on bf16 inputs: Q and K
  *           are rotated by a fixed random-sign Hadamard matrix and all three
  *           are block-quantised to e4m3, then the fa_fwd_fp8 kernel runs.
