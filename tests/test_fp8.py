@@ -77,9 +77,9 @@ def check_codes(codes_gpu, codes_ref, t_exact, t_err):
     t_err of the midpoint between the two codes' values (the kernel's own
     scaled value may then round to the other side). bf16 inputs have 8
     significant bits, so such near-ties are far more frequent than for
-    continuous values (about 1e-3 of the outlier workload's codes): their
-    number is printed beside the number of codes that differ, which may not
-    exceed it (nor 1% of the codes)."""
+    continuous values (up to a few per thousand of the outlier workload's
+    codes): their number is printed beside the number of codes that differ,
+    which may not exceed it (nor 1% of the codes)."""
     a = fp8.e4m3_decode(codes_gpu)
     b = fp8.e4m3_decode(codes_ref)
     diff = a != b
