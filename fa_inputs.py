@@ -20,6 +20,12 @@ Workloads (all synthetic; the pages measure on synthetic data themselves):
   * an upstream gradient dO for the backward pass: iid N(0,1) entries of the
     output's shape, rounded to bf16 (the pages give no distribution for it;
     this is the plainest choice, the same as the inputs').
+  * a structured workload (not on the pages) whose scores grow along the key
+    axis: iid N(0,1) entries, then column 0 of Q set to a constant and column
+    0 of K to a ramp over the key positions, rounded to bf16. Every row's
+    running maximum then moves several times over the sequence, which iid
+    inputs do only at the first key tile: it exercises the rescaling of the
+    online softmax.
   * for tensors of more than 2^31 elements (the size-limit tests), iid N(0,1)
     entries drawn on the device by torch's seeded generator and rounded to
     bf16 there; the oracle receives the bf16 patterns of the heads it checks,
@@ -88,6 +94,20 @@ class QKV:
 
 def make_qkv(B, H, N, d, seed, dist="normal") -> QKV:
     return QKV(B, H, N, d, seed, dist)
+
+
+def make_qkv_ramp(B, H, N, d, seed, q0, amp) -> QKV:
+    """make_qkv's iid N(0,1) Q, K, V, then Q[..., n, 0] = q0 for every row
+    and K[..., j, 0] = amp * j / N at key position j (both rounded to bf16)."""
+    g = QKV(B, H, N, d, seed)
+    q = g.q.astype(np.float32)
+    k = g.k.astype(np.float32)
+    q[..., 0] = np.float32(q0)
+    k[..., 0] = (float(amp) * np.arange(N, dtype=np.float64) / N).astype(np.float32)
+    g.q_bits = bf16_bits(q)
+    g.k_bits = bf16_bits(k)
+    g.dist = "ramp"
+    return g
 
 
 def make_grad(B, H, N, d, seed):

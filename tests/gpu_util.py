@@ -18,6 +18,14 @@ LSE_MAX_ABS = 1e-3
 FP8_REL_RMSE = 5e-2
 
 
+def ramp_amp(d, growth_log2, q0=4.0):
+    """Height of the key ramp of fa_inputs.make_qkv_ramp (column 0 of Q set
+    to q0) that makes the scores, at scale 1/sqrt(d), grow by about
+    growth_log2 log2 units from the first key to the last."""
+    import math
+    return growth_log2 * math.sqrt(d) / (math.log2(math.e) * q0)
+
+
 def half_ulp_bf16(x):
     """Half the spacing of bf16 values at |x| (8 significant bits)."""
     a = np.abs(np.asarray(x, dtype=np.float64))

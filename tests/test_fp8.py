@@ -29,7 +29,7 @@ import pytest
 import fa_inputs
 from oracle import attention, fp8
 from tests.fp8_gate import fp8_gate, fp8_reference_and_bounds
-from tests.gpu_util import FP8_REL_RMSE, oracle_full
+from tests.gpu_util import FP8_REL_RMSE, oracle_full, ramp_amp
 
 pytestmark = pytest.mark.gpu
 
@@ -231,9 +231,9 @@ def structured_v(kind, v):
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_fp8_structured_v_scales(lib, kind, d, causal):
     """V block scales far apart within one head: the V fold keeps every
-    tile's P * 2^8 * r above 2^4 * P (the reference V scale moves when the
-    ratio leaves [2^-4, 1]), so these cases meet the same rounding bound as
-    the plain workload, and rows that never reach the zero block stay
+    tile's P * 2^6 * r at or above 2^2 * P (the reference V scale moves when
+    the ratio leaves [2^-4, 1]), so these cases meet the same rounding bound
+    as the plain workload, and rows that never reach the zero block stay
     finite."""
     announce("fwd fp8 structured V", kind, d, causal)
     B, H, N = 1, 2, 384
@@ -245,6 +245,25 @@ def test_fwd_fp8_structured_v_scales(lib, kind, d, causal):
     vc, sv = fp8.quantize(v)
     announce("  V block scales", sv[0, 0].tolist())
     o_ref, _ = attention(g.q, g.k, v, causal)
+    check_fwd_fp8(lib, (qc, kc, vc), (sq, sk, sv), causal, 1.0 / math.sqrt(d), exact=o_ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_running_max_moves(lib, causal):
+    """Scores growing along the key axis (fa_inputs.make_qkv_ramp, about 8.5
+    log2 units every 256 keys; Q and K rotated): the e4m3 kernel's reference
+    maximum, with its 2.75 log2-unit window, moves at most key tiles, each
+    move rescaling the accumulator and the row sum; K's block scales grow
+    along the sequence. Gated against exact attention on the dequantised
+    operands like the other cases."""
+    announce("fwd fp8 ramp", causal)
+    B, H, N, d = 1, 2, 1000, 128
+    g = fa_inputs.make_qkv_ramp(B, H, N, d, 780 + causal, 4.0, ramp_amp(d, 8.5 * N / 256))
+    signs = fa_inputs.random_signs(d, 781)
+    qc, sq = fp8.quantize(g.q, signs=signs)
+    kc, sk = fp8.quantize(g.k, signs=signs)
+    vc, sv = fp8.quantize(g.v)
+    o_ref, _ = attention(g.q, g.k, g.v, causal)
     check_fwd_fp8(lib, (qc, kc, vc), (sq, sk, sv), causal, 1.0 / math.sqrt(d), exact=o_ref)
 
 

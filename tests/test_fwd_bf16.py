@@ -12,7 +12,7 @@ import pytest
 
 import fa_inputs
 from oracle import attention
-from tests.gpu_util import (LSE_MAX_ABS, bf16_gate, oracle_full, run_bf16,
+from tests.gpu_util import (LSE_MAX_ABS, bf16_gate, oracle_full, ramp_amp, run_bf16,
                             to_device)
 
 pytestmark = pytest.mark.gpu
@@ -22,9 +22,11 @@ def announce(*args):
     print("[case]", *args, file=sys.stderr, flush=True)
 
 
-def check_full(fa, B, H, N, d, causal, seed, dist="normal"):
-    announce("full", B, H, N, d, "causal" if causal else "noncausal", "seed", seed)
-    g = fa_inputs.make_qkv(B, H, N, d, seed, dist)
+def check_full(fa, B, H, N, d, causal, seed, dist="normal", g=None):
+    announce("full", B, H, N, d, "causal" if causal else "noncausal", "seed", seed,
+             g.dist if g is not None else dist)
+    if g is None:
+        g = fa_inputs.make_qkv(B, H, N, d, seed, dist)
     o_gpu, lse_gpu = run_bf16(fa, g, causal)
     o_ref, lse_ref = attention(g.q, g.k, g.v, causal)
     ok, st = bf16_gate(o_gpu, o_ref)
@@ -258,3 +260,30 @@ def test_few_heads_long_sequence(lib, causal):
         # 160 query tiles: causal shapes up to 224 take the split path
         # (5 splits), non-causal ones the one-pass kernel
         check_full(lib, 1, 5, 4096, 128, causal, 20003)
+
+
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_moves(lib, d, causal):
+    """Scores that grow along the key axis (fa_inputs.make_qkv_ramp, about 8.5
+    log2 units every 256 keys): the reference maximum of every wave moves
+    past the kernel's lazy threshold several times, so O and l are rescaled
+    by factors strictly between 0 and 1, which iid inputs never cause after
+    the first tile (tests/test_workloads.py: the same inputs catch a wrong
+    rescale factor in an fp64 emulation by a wide margin). N = 1000 also
+    ends in a partial tile."""
+    N = 1000
+    g = fa_inputs.make_qkv_ramp(1, 2, N, d, 21000 + d + causal, 4.0,
+                                ramp_amp(d, 8.5 * N / 256))
+    check_full(lib, 1, 2, N, d, causal, g.seed, g=g)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_moves_split_route(lib, causal):
+    """The ramp workload on a few-heads shape that fa_fwd runs in the forward
+    kernel's split mode: each split's running maximum moves, and the splits'
+    log-sum-exps differ by tens of units before the merge."""
+    N = 4096
+    g = fa_inputs.make_qkv_ramp(1, 2, N, 128, 21300 + causal, 4.0,
+                                ramp_amp(128, 8.5 * N / 256))
+    check_full(lib, 1, 2, N, 128, causal, g.seed, g=g)

@@ -12,7 +12,7 @@ import pytest
 
 import fa_inputs
 from oracle import attention_kv
-from tests.gpu_util import LSE_MAX_ABS, bf16_gate
+from tests.gpu_util import LSE_MAX_ABS, bf16_gate, ramp_amp
 
 pytestmark = pytest.mark.gpu
 
@@ -21,9 +21,15 @@ def announce(*args):
     print("[case]", *args, file=sys.stderr, flush=True)
 
 
-def make(B, H, Nq, Nk, d, seed):
-    g = fa_inputs.make_qkv(B, H, Nk, d, seed)           # K, V (and an unused Q)
-    gq = fa_inputs.make_qkv(B, H, Nq, d, seed + 50000)  # Q
+def make(B, H, Nq, Nk, d, seed, ramp=False):
+    if ramp:
+        # scores growing along the key axis, about 8.5 log2 units every 256 keys
+        amp = ramp_amp(d, 8.5 * Nk / 256)
+        g = fa_inputs.make_qkv_ramp(B, H, Nk, d, seed, 4.0, amp)
+        gq = fa_inputs.make_qkv_ramp(B, H, Nq, d, seed + 50000, 4.0, amp)
+    else:
+        g = fa_inputs.make_qkv(B, H, Nk, d, seed)           # K, V (and an unused Q)
+        gq = fa_inputs.make_qkv(B, H, Nq, d, seed + 50000)  # Q
     return gq.q_bits, g.k_bits, g.v_bits
 
 
@@ -36,10 +42,11 @@ def run(fa, qb, kb, vb, causal, splits, scale=None):
             lse.cpu().numpy().astype(np.float64))
 
 
-def check(fa, B, H, Nq, Nk, d, causal, splits, seed, scale=None):
+def check(fa, B, H, Nq, Nk, d, causal, splits, seed, scale=None, ramp=False):
     announce("splitkv", B, H, Nq, Nk, d, "causal" if causal else "noncausal", "splits", splits,
-             "(used", fa.splitkv_splits(B, H, Nq, Nk, splits, causal), ") seed", seed)
-    qb, kb, vb = make(B, H, Nq, Nk, d, seed)
+             "(used", fa.splitkv_splits(B, H, Nq, Nk, splits, causal), ") seed", seed,
+             "ramp" if ramp else "")
+    qb, kb, vb = make(B, H, Nq, Nk, d, seed, ramp)
     o, lse = run(fa, qb, kb, vb, causal, splits, scale)
     o_ref, lse_ref = attention_kv(*(fa_inputs.bf16_bits_to_f64(x) for x in (qb, kb, vb)), causal,
                                   scale)
@@ -138,3 +145,22 @@ def test_deterministic(lib):
     for o, lse in runs[1:]:
         assert torch.equal(o.view(torch.int16), runs[0][0].view(torch.int16))
         assert torch.equal(lse, runs[0][1])
+
+
+RAMP_CASES = [
+    # (B, H, Nq, Nk, d, causal, splits)
+    (2, 2, 1, 4100, 128, False, 0),     # decode
+    (1, 2, 16, 4100, 96, True, 0),
+    (1, 2, 1500, 1500, 128, True, 4),   # Nq == Nk: the forward kernel's split mode
+    (1, 2, 1500, 1500, 64, False, 3),
+]
+
+
+@pytest.mark.parametrize("case", RAMP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_splitkv_running_max_moves(lib, case):
+    """Scores growing along the key axis (fa_inputs.make_qkv_ramp): inside a
+    split the running maximum moves several times, and the splits'
+    log-sum-exps differ by tens of units, so the merge weights span many
+    orders of magnitude."""
+    B, H, Nq, Nk, d, causal, splits = case
+    check(lib, B, H, Nq, Nk, d, causal, splits, 22000 + Nq + d, ramp=True)
