@@ -86,6 +86,50 @@ def bwd_gate(g_gpu, g_ref, extra=None):
     return ok, stats
 
 
+def bwd_rounding_bound(q, k, v, do, o, lse, causal, scale):
+    """Elementwise bound on |G - R| for the backward of one head (float64
+    [N, d] arrays; o and lse as the backward was given them), R the gradient
+    with D formed from that o, derived from the kernels' arithmetic rather
+    than from a workload: S = Q K^T, dP = dO V^T and D = rowsum(dO * O) are
+    float32 sums of exact products, P = exp2(scale*log2e*S - LSE*log2e) and
+    dS = P (dP - D) are formed in float32, then P and dS are rounded to bf16
+    (8 significant bits: relative error <= 2^-8) as operands of
+    dV = P^T dO, dK = scale dS^T Q and dQ = scale dS K, which accumulate in
+    float32. The rounding of G to bf16 is not included (the caller adds half
+    an ulp). Where dQ comes from cancellation (sum_j dS_ij = 0 against large
+    K rows) this allows more than the relative gate of the iid workloads.
+    Returns (bound_dq, bound_dk, bound_dv)."""
+    n, d = q.shape
+    u = 2.0 ** -24
+    log2e = 1.4426950408889634
+    s = scale * (q @ k.T)
+    mask = np.arange(n)[None, :] > np.arange(n)[:, None] if causal else None
+    if mask is not None:
+        s = np.where(mask, -np.inf, s)
+    p = np.exp(s - lse[:, None])
+    dp = do @ v.T
+    dr = (do * o).sum(axis=1)
+    ds = p * (dp - dr[:, None])
+    # float32 error of P: its exp2 argument is a difference of terms of size
+    # scale*log2e*sum|q||k| and |LSE|*log2e, each formed with at most d + 2
+    # roundings; exp2 itself adds about one ulp
+    arg = (d + 2) * u * (scale * log2e * (np.abs(q) @ np.abs(k).T) + log2e * np.abs(lse)[:, None])
+    eps_p = np.log(2.0) * arg + 4 * u
+    err_dp = d * u * (np.abs(do) @ np.abs(v).T)
+    err_dr = d * u * (np.abs(do) * np.abs(o)).sum(axis=1)
+    ds32 = np.abs(ds) * (eps_p + 2 * u) + p * (1 + eps_p) * (err_dp + err_dr[:, None])
+    e_ds = 2.0 ** -8 * (np.abs(ds) + ds32) + ds32
+    e_p = 2.0 ** -8 * p * (1 + eps_p) + p * eps_p
+    if mask is not None:
+        e_ds = np.where(mask, 0.0, e_ds)
+        e_p = np.where(mask, 0.0, e_p)
+    acc = n * u   # float32 accumulation over at most n terms
+    bq = scale * (e_ds @ np.abs(k) + acc * (np.abs(ds) @ np.abs(k)))
+    bk = scale * (e_ds.T @ np.abs(q) + acc * (np.abs(ds).T @ np.abs(q)))
+    bv = e_p.T @ np.abs(do) + acc * (p.T @ np.abs(do))
+    return bq, bk, bv
+
+
 def oracle_fwd_inputs(g, causal, scale=None):
     """The forward output the backward is handed, from the oracle: O rounded
     to bf16 (the forward's output format) and LSE rounded to float32.

@@ -1,5 +1,7 @@
 """CPU checks of the structured ramp workload (fa_inputs.make_qkv_ramp) that
-the GPU tests use to exercise the online softmax's rescaling.
+the GPU tests use to exercise the online softmax's rescaling, and of the
+backward's rounding bound (tests/gpu_util.bwd_rounding_bound) that gates the
+backward on it.
 
 With iid N(0,1) inputs a row's running maximum settles at the first key tile:
 a kernel whose rescale factor were wrong would still pass every iid case. The
@@ -22,8 +24,8 @@ import numpy as np
 import pytest
 
 import fa_inputs
-from oracle import attention
-from tests.gpu_util import bf16_gate, ramp_amp
+from oracle import attention, attention_backward
+from tests.gpu_util import bf16_gate, bwd_rounding_bound, half_ulp_bf16, ramp_amp
 
 LOG2E = 1.4426950408889634
 N, D = 1000, 128
@@ -99,3 +101,48 @@ def test_iid_inputs_settle_at_the_first_tile():
     g = fa_inputs.make_qkv(1, 1, N, D, 21129)
     _, moves, partial = lazy_softmax(g.q[0, 0], g.k[0, 0], g.v[0, 0], False)
     assert max(moves) == 1 and partial == 0
+
+
+def _bf16(x):
+    return fa_inputs.bf16_bits_to_f64(fa_inputs.bf16_bits(np.asarray(x, dtype=np.float32)))
+
+
+def _backward_bound_ratio(g, do, causal, drop_tile=False):
+    """Worst ratio of |G - R| to the rounding bound (plus half an ulp of the
+    output) over one head, G from an fp64 emulation of the backward's
+    roundings (P and dS to bf16 as operands, each gradient to bf16), R the
+    oracle's gradient with D from the bf16 O."""
+    n, d = g.q.shape[2], g.q.shape[3]
+    scale = 1.0 / math.sqrt(d)
+    o, lse = attention(g.q, g.k, g.v, causal)
+    ob = _bf16(o)
+    lse32 = lse.astype(np.float32).astype(np.float64)
+    ref = attention_backward(g.q, g.k, g.v, do, causal, o=ob)
+    q, k, v, dO = g.q[0, 0], g.k[0, 0], g.v[0, 0], do[0, 0]
+    s = scale * (q @ k.T)
+    if causal:
+        s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+    p = np.exp(s - lse32[0, 0][:, None])
+    ds = p * (dO @ v.T - (dO * ob[0, 0]).sum(axis=1)[:, None])
+    if drop_tile:   # a planted mistake: one key tile's contributions lost
+        p[:, 64:128] = 0.0
+        ds[:, 64:128] = 0.0
+    got = (_bf16(scale * (_bf16(ds) @ k)), _bf16(scale * (_bf16(ds).T @ q)), _bf16(_bf16(p).T @ dO))
+    bounds = bwd_rounding_bound(q, k, v, dO, ob[0, 0], lse32[0, 0], causal, scale)
+    worst = 0.0
+    for x, r, b in zip(got, (ref[0][0, 0], ref[1][0, 0], ref[2][0, 0]), bounds):
+        allowed = b + half_ulp_bf16(np.abs(r) + b) + 1e-7
+        worst = max(worst, float((np.abs(x - r) / allowed).max()))
+    return worst
+
+
+@pytest.mark.parametrize("ramp", [False, True])
+def test_backward_rounding_bound(ramp):
+    """The emulated roundings stay inside the bound (causal, the tighter
+    mask), and a dropped key tile leaves it by far."""
+    n, d = (640, 64) if ramp else (300, 64)
+    g = (fa_inputs.make_qkv_ramp(1, 1, n, d, 9765, 4.0, ramp_amp(d, 8.5 * n / 256)) if ramp
+         else fa_inputs.make_qkv(1, 1, n, d, 9064))
+    _, do = fa_inputs.make_grad(1, 1, n, d, 9766)
+    assert _backward_bound_ratio(g, do, True) < 1.0
+    assert _backward_bound_ratio(g, do, True, drop_tile=True) > 10.0
