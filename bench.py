@@ -164,6 +164,40 @@ def extras(fa, only=None):
         out.append(rec)
         del q, k, v, o, lse
 
+    def run_cold(name, B, H, N, d, causal, seed, trials=21):
+        """Secondary, cold-cache timing: a 1 GiB device write before each
+        call evicts L2 and the MALL, so Q, K and V come from HBM; the median
+        of `trials` single calls, each bracketed by HIP events after the
+        write."""
+        if not want(name):
+            return
+        q, k, v = device_qkv(B, H, N, d, seed)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        call = lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+        settle(call, 3)
+        times = []
+        for i in range(trials):
+            scrub.fill_(i & 0xFF)
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            call()
+            end.record()
+            torch.cuda.synchronize()
+            times.append(start.elapsed_time(end))
+        ms = sorted(times)[len(times) // 2]
+        tf = flops(B, H, N, d, causal) / (ms * 1e-3) / 1e12
+        out.append({"name": name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                    "dtype": "bf16", "cache": "cold: 1 GiB write before each call, median of "
+                    f"{trials}", "ms": round(ms, 4), "tflops": round(tf, 1),
+                    "pct_peak": round(100 * tf / PEAK_BF16, 1)})
+        del q, k, v, o, lse, scrub
+
+    for causal in (False, True):
+        run_cold("cold-cache mid", 4, 16, 2048, 128, causal, fa_inputs.SEEDS["mid"])
+    run_cold("cold-cache headline", 1, 16, 16384, 128, False, fa_inputs.SEEDS["seq_sweep_base"] + 5)
+
     # decode against a 16k-token cache, one and sixteen new queries per (b, h)
     for causal in (False, True):
         run_split("decode split-KV (fa_fwd_splitkv)", 4, 16, 1, 16384, 128, causal, 13000)
