@@ -635,10 +635,19 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
 
   // KIND: 0 = steady state (tile t+1 needs no mask), 1 = tile t+1 may need
   // masking, 2 = last tile (t = T-1): there is no tile t+1 to score or copy.
-  auto step = [&](auto kind_tag, const char* kr, const char* vr, char* kl, char* vl, int t) {
+  // The per-block factors of the tile (one quantisation block spans two
+  // tiles): read at the even tile of a block, reused at the odd one.
+  float cs_blk = 0.f, sv_blk = 1.f, isv_blk = 1.f, l2_blk = 0.f;
+  auto step = [&](auto kind_tag, auto odd_tag, const char* kr, const char* vr, char* kl,
+                  char* vl, int t) {
     constexpr int KIND = decltype(kind_tag)::value;
     constexpr bool MASK = KIND == 1;
     constexpr bool LAST = KIND == 2;
+    // ODD: tile t is the second tile of its block and the previous step
+    // handled the first, with the same factors; the V reference then already
+    // lies within its window (it either stayed or moved to this block's
+    // scale), so the move check is skipped.
+    constexpr bool ODD = decltype(odd_tag)::value;
     // Tile t lies in key block t / 2 (kBC = 64, kBlock = 128); a new table
     // is loaded before the wait below, which also covers these loads.
     static_assert(kBlock == 2 * kBC, "two key tiles per quantisation block");
@@ -650,24 +659,26 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
       cp.issue(rk, kl, (t + 2) * kBC, wave, t + 2 < T);
       cp.issue(rv, vl, (t + 1) * kBC, wave, t + 1 < T);
     }
-    float cs, sv_t, isv_t, l2_t;
-    if constexpr (kTable) {
-      cs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_cs), blk & 63));
-      sv_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_sv), blk & 63));
-      isv_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_isv), blk & 63));
-      l2_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_l2sv), blk & 63));
-    } else {
-      cs = c * sq * skh[blk];
-      sv_t = pos_sv(svh[blk]);
-      isv_t = 1.f / sv_t;
-      l2_t = __log2f(sv_t);
+    if constexpr (!ODD) {
+      if constexpr (kTable) {
+        cs_blk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_cs), blk & 63));
+        sv_blk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_sv), blk & 63));
+        isv_blk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_isv), blk & 63));
+        l2_blk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tab_l2sv), blk & 63));
+      } else {
+        cs_blk = c * sq * skh[blk];
+        sv_blk = pos_sv(svh[blk]);
+        isv_blk = 1.f / sv_blk;
+        l2_blk = __log2f(sv_blk);
+      }
     }
+    const float cs = cs_blk, sv_t = sv_blk, isv_t = isv_blk, l2_t = l2_blk;
     // 1 / r_t = sv_ref / sv_t (IEEE products: the accumulator's scaling and
     // the row sum use these; the fold factor inside exp2 only needs to be
     // close, its error cancels between P V and the row sum). The reference
     // moves when r_t > 1 (beyond rounding) or r_t < 2^-4.
     float inv_r = sv_ref * isv_t;
-    const bool vmove = inv_r < kVLow || inv_r > kVHigh;
+    const bool vmove = !ODD && (inv_r < kVLow || inv_r > kVHigh);
     const float mx = mt * cs;
     if (__any(vmove || mx - m_ref > kLazy)) {
       // New reference maximum (per lane) and, if the V fold ratio left its
@@ -761,22 +772,24 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   using Steady = std::integral_constant<int, 0>;
   using Masked = std::integral_constant<int, 1>;
   using Last = std::integral_constant<int, 2>;
+  using Even = std::false_type;
+  using Odd = std::true_type;
   int t = 0;
   for (; t + 2 < J; t += 2) {  // steps whose next tile (t+1, t+2) is unmasked
-    step(Steady{}, ks1, vs0, ks0, vs1, t);
-    step(Steady{}, ks0, vs1, ks1, vs0, t + 1);
+    step(Steady{}, Even{}, ks1, vs0, ks0, vs1, t);
+    step(Steady{}, Odd{}, ks0, vs1, ks1, vs0, t + 1);
   }
   for (; t + 2 < T; t += 2) {  // t is even here: stage parity stays static
-    step(Masked{}, ks1, vs0, ks0, vs1, t);
-    step(Masked{}, ks0, vs1, ks1, vs0, t + 1);
+    step(Masked{}, Even{}, ks1, vs0, ks0, vs1, t);
+    step(Masked{}, Odd{}, ks0, vs1, ks1, vs0, t + 1);
   }
   if (t + 1 < T) {  // two tiles left
-    step(Masked{}, ks1, vs0, ks0, vs1, t);
+    step(Masked{}, Even{}, ks1, vs0, ks0, vs1, t);
     ++t;
   }
   // The last step only finishes tile t (reads V_t); one call site with the
   // stage chosen at run time.
-  step(Last{}, ks0, (t & 1) ? vs1 : vs0, ks1, (t & 1) ? vs0 : vs1, t);
+  step(Last{}, Even{}, ks0, (t & 1) ? vs1 : vs0, ks1, (t & 1) ? vs0 : vs1, t);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // no copy lands after the exit
 
   // Stage the output rows through LDS (whole-row stores): once every wave
