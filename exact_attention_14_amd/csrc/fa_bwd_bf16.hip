@@ -454,7 +454,7 @@ hipError_t bwd_launch(const void* q, const void* k, const void* v, const void* o
                      lse, nl, dvec, (u16*)dq, N, nt, nwg_arg, hpx, scale);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream,
                      (const u16*)q, (const u16*)k, (const u16*)v, (const u16*)dout,
-                     (const float*)nl, (const float*)dvec, (u16*)dk, (u16*)dv, N, nt, (int)nwg,
+                     (const float*)nl, (const float*)dvec, (u16*)dk, (u16*)dv, N, nt, nwg_arg,
                      hpx, scale);
   return hipGetLastError();
 }

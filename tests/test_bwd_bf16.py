@@ -140,6 +140,32 @@ def test_deterministic(lib):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+def test_grid_order_bitwise(lib):
+    """Both backward kernels with their workgroups in reverse order (and
+    without the per-XCD head grouping; FA_DEBUG=1) give the default order's
+    gradients bit for bit: every gradient row has one writer and no result
+    depends on which workgroups run first."""
+    import os
+    import torch
+    from tests.gpu_util import to_device
+    for causal in (False, True):
+        announce("bwd grid order 2 8 1000 128", "causal" if causal else "noncausal")
+        g = fa_inputs.make_qkv(2, 8, 1000, 128, 80 + causal)
+        do_bits, _ = fa_inputs.make_grad(2, 8, 1000, 128, 82 + causal)
+        q, k, v = to_device(g)
+        do = fa_inputs.to_torch_bf16(do_bits, "cuda")
+        o, lse = lib.fwd(q, k, v, causal=causal)
+        a = lib.bwd(q, k, v, o, lse, do, causal=causal)
+        os.environ["FA_DEBUG"] = "1"
+        try:
+            b = lib.bwd(q, k, v, o, lse, do, causal=causal)
+        finally:
+            del os.environ["FA_DEBUG"]
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
 def test_scale_argument(lib):
     # a scale other than 1/sqrt(d) reaches the backward
     check_bwd(lib, 1, 2, 200, 64, True, 79, scale=0.3)
