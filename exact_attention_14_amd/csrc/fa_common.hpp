@@ -177,12 +177,9 @@ __device__ __forceinline__ void poison_lds(char* p, int bytes, int tid, int nthr
 // XCDs round-robin. With hpx > 0 (B*H = 8*hpx heads) each XCD owns hpx whole
 // heads and starts its workgroups in rank order across them (rank 0 = the
 // longest causal tile first); otherwise consecutive logical ids, i.e. the
-// tiles of one head, run on one XCD. `nwg` may carry debug flags in its top
-// bits (kDbgReverse: logical id nwg - 1 - bid).
-__device__ __forceinline__ void tile_of_workgroup(int bid, int nwg, int ntq, int hpx, int& bh,
-                                                  int& rank) {
-  if (dbg_flags(nwg) & kDbgReverse) bid = (nwg & ((1 << kDbgShift) - 1)) - 1 - bid;
-  nwg &= (1 << kDbgShift) - 1;
+// tiles of one head, run on one XCD. `nwg` is the plain workgroup count.
+__device__ __forceinline__ void tile_of_id(int bid, int nwg, int ntq, int hpx, int& bh,
+                                           int& rank) {
   if (hpx > 0) {
     const int loc = bid >> 3;
     rank = loc / hpx;
@@ -194,6 +191,14 @@ __device__ __forceinline__ void tile_of_workgroup(int bid, int nwg, int ntq, int
   const int lid = xcd < r8 ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
   rank = lid % ntq;
   bh = lid / ntq;
+}
+
+// The same for grids below 2^24 workgroups whose count argument carries the
+// debug flags in its top bits (kDbgReverse: logical id nwg - 1 - bid).
+__device__ __forceinline__ void tile_of_workgroup(int bid, int nwg, int ntq, int hpx, int& bh,
+                                                  int& rank) {
+  if (dbg_flags(nwg) & kDbgReverse) bid = (nwg & ((1 << kDbgShift) - 1)) - 1 - bid;
+  tile_of_id(bid, nwg & ((1 << kDbgShift) - 1), ntq, hpx, bh, rank);
 }
 
 

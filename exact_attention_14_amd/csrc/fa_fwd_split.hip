@@ -41,7 +41,7 @@ template <int D, bool CAUSAL, int NW, int KT, int S>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_split_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     float* __restrict__ Op, float* __restrict__ Lp, int Nq, int Nk, int nqt, int splits, int tps,
-    int nwg, float scale) {
+    int nwg, float scale, int dbg) {
   using G = Geo<D>;
   using CP = TileCopy<D, NW, KT>;
   static_assert(KT == 32 || KT == 64, "32- or 64-key tiles");
@@ -66,16 +66,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // when B*H divides 8 or 8 divides B*H), then query tiles from the last,
   // their splits consecutive. Grouping a head's items on one die would give
   // the die of its last query tiles most of the work.
+  // dbg (kDbgReverse, kDbgPoison): the debug order and LDS poison of the
+  // forward kernels, passed apart from nwg: one-wave workgroups make this
+  // grid reach 2^26, past the bits the other kernels leave for the flags.
+  const unsigned bid = (dbg & kDbgReverse) ? (unsigned)nwg - 1u - blockIdx.x : blockIdx.x;
   int bh, sp, qt;
   if constexpr (CAUSAL && NW > 1) {
     const int bht = nwg / (nqt * splits);
-    bh = (int)(blockIdx.x % (unsigned)bht);
-    const int rank = (int)(blockIdx.x / (unsigned)bht);
+    bh = (int)(bid % (unsigned)bht);
+    const int rank = (int)(bid / (unsigned)bht);
     qt = nqt - 1 - rank / splits;
     sp = rank % splits;
   } else {
     int rank;
-    tile_of_workgroup(blockIdx.x, nwg, nqt * splits, 0, bh, rank);
+    tile_of_id((int)bid, nwg, nqt * splits, 0, bh, rank);
     sp = rank / nqt;
     qt = rank % nqt;
   }
@@ -120,6 +124,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // wait for the copies issued ahead there.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
+  if (dbg & kDbgPoison) {
+    poison_lds(ring, (int)sizeof(ring), tid, 64 * NW);
+    __syncthreads();
+  }
   const CP cp(wave, lane);
   auto issue = [&](int t) {
     char* const st = ring + ((t - t_begin) % S) * (2 * TB);
@@ -395,7 +403,7 @@ hipError_t split_launch(const void* q, const void* k, const void* v, void* o, fl
   } else {
     hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL, NW, KT, S>), dim3((unsigned)nwg),
                        dim3(64 * NW), 0, stream, (const u16*)q, (const u16*)k, (const u16*)v, op,
-                       lp, Nq, Nk, nqt, splits, tps, (int)nwg, scale);
+                       lp, Nq, Nk, nqt, splits, tps, (int)nwg, scale, debug_flags());
   }
   if (splits >= kMergeGroups) {
     hipLaunchKernelGGL((split_combine_rows_kernel<D>), dim3((unsigned)rows),

@@ -161,3 +161,41 @@ def test_splitkv_past_2_31_elements(lib, big, Nq, causal, splits):
     announce("  stats", st, "lse_max_abs", lse_err)
     assert ok, st
     assert lse_err <= LSE_MAX_ABS
+
+
+def test_decode_grid_past_2_24_workgroups(lib):
+    """Decode over B*H = 2^24 + 1024 heads (one query, two keys each, d = 64):
+    the split-KV kernel runs one single-wave workgroup per head, a grid past
+    the 2^24 workgroups below which the other kernels carry debug flags in
+    their workgroup-count argument; the heads around 2^24, the first and last
+    and three at random are checked against the oracle."""
+    import torch
+    Bd, Hd, Nk, d = 16385, 1024, 2, 64
+    nheads = Bd * Hd
+    assert nheads > (1 << 24) and lib.splitkv_splits(Bd, Hd, 1, Nk) == 1
+    announce("decode grid past 2^24 workgroups", Bd, Hd, 1, Nk, d)
+    seed = fa_inputs.SEEDS["large"] + 10
+    q = fa_inputs.device_normal_bf16((Bd, Hd, 1, d), seed)
+    k = fa_inputs.device_normal_bf16((Bd, Hd, Nk, d), seed + 1)
+    v = fa_inputs.device_normal_bf16((Bd, Hd, Nk, d), seed + 2)
+    o, lse = lib.fwd_splitkv(q, k, v)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    flat = [0, 1, (1 << 24) - 1, 1 << 24, (1 << 24) + 1, nheads - 1]
+    flat += [int(x) for x in rng.integers(0, nheads, 3)]
+    picks = [divmod(f, Hd) for f in flat]
+
+    def rows(t):
+        return np.stack([fa_inputs.bf16_bits_to_f64(fa_inputs.bf16_tensor_to_bits(t[b, h]))
+                         for b, h in picks])
+
+    got, qh, kh, vh = rows(o), rows(q), rows(k), rows(v)
+    got_lse = np.stack([lse[b, h].cpu().numpy().astype(np.float64) for b, h in picks])
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    ref, ref_lse = attention_kv(qh[None], kh[None], vh[None], False)
+    ok, st = bf16_gate(got, ref[0])
+    lse_err = float(np.abs(got_lse - ref_lse[0]).max())
+    announce("  stats", st, "lse_max_abs", lse_err)
+    assert ok, st
+    assert lse_err <= LSE_MAX_ABS
