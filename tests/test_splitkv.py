@@ -147,6 +147,32 @@ def test_deterministic(lib):
         assert torch.equal(lse, runs[0][1])
 
 
+@pytest.mark.parametrize("case", [(2, 4, 1, 4100, 128, True, 0), (1, 3, 257, 1000, 96, True, 4),
+                                  (2, 2, 7, 300, 64, False, 3)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_grid_order_and_lds_poison_bitwise(lib, case):
+    """The split kernel with its workgroups in reverse order and its LDS ring
+    filled with NaN bytes before the first copy (FA_DEBUG=3) gives the
+    default run's output bit for bit: decode (one wave per workgroup, 32-key
+    tiles) and queries of another length than the keys (four waves, 64-key
+    tiles)."""
+    import os
+    import torch
+    B, H, Nq, Nk, d, causal, splits = case
+    announce("splitkv grid order / lds poison", *case)
+    qb, kb, vb = make(B, H, Nq, Nk, d, 12100 + Nq)
+    q, k, v = (fa_inputs.to_torch_bf16(x, "cuda") for x in (qb, kb, vb))
+    a = lib.fwd_splitkv(q, k, v, causal=causal, num_splits=splits)
+    os.environ["FA_DEBUG"] = "3"
+    try:
+        b = lib.fwd_splitkv(q, k, v, causal=causal, num_splits=splits)
+    finally:
+        del os.environ["FA_DEBUG"]
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
+
+
 RAMP_CASES = [
     # (B, H, Nq, Nk, d, causal, splits)
     (2, 2, 1, 4100, 128, False, 0),     # decode
