@@ -119,6 +119,21 @@ def _check_buf(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be on {device}, got {t.device}")
 
 
+def _no_overlap(outputs, inputs):
+    """Outputs must not share memory with the inputs (nor with each other):
+    the kernels read the inputs while other workgroups write the outputs."""
+    def span(t):
+        return t.data_ptr(), t.data_ptr() + t.numel() * t.element_size()
+    outs = [(n, t) for n, t in outputs if t is not None]
+    ins = [(n, t) for n, t in inputs if t is not None]
+    for i, (no, to) in enumerate(outs):
+        a0, a1 = span(to)
+        for ni, ti in ins + outs[i + 1:]:
+            b0, b1 = span(ti)
+            if a0 < b1 and b0 < a1:
+                raise ValueError(f"{no} overlaps {ni} in memory")
+
+
 def _check_qkv(q, k, v, dtype):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -148,6 +163,7 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, dtype: int = 
         scale = 1.0 / math.sqrt(d)
     _check_buf(out, "out", q.shape, torch.bfloat16, q.device)
     _check_buf(lse, "lse", (B, H, N), torch.float32, q.device)
+    _no_overlap((("out", out), ("lse", lse)), (("q", q), ("k", k), ("v", v)))
     o = torch.empty_like(q) if out is None else out
     if lse is None and return_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -168,6 +184,7 @@ def quant_fp8(x, per_tensor: bool = False, signs=None, out=None, scales=None):
     _check_buf(out, "out", x.shape, torch.float8_e4m3fn, x.device)
     _check_buf(scales, "scales", (B, H, nblk), torch.float32, x.device)
     _check_buf(signs, "signs", (d,), torch.float32, x.device)
+    _no_overlap((("out", out), ("scales", scales)), (("x", x), ("signs", signs)))
     x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device) if out is None else out
     sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device) if scales is None else scales
     _launch(lib.fa_quant_fp8, "fa_quant_fp8", x.device, _ptr(x), _ptr(x8), _ptr(sc), B, H, N, d,
@@ -189,6 +206,8 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = 
     _check_buf(lse, "lse", (B, H, N), torch.float32, q8.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _no_overlap((("out", out), ("lse", lse)),
+                (("q8", q8), ("k8", k8), ("v8", v8), ("sq", sq), ("sk", sk), ("sv", sv)))
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
     if lse is None and return_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
@@ -215,6 +234,7 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
     _check_buf(lse, "lse", (B, H, Nq), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _no_overlap((("out", out), ("lse", lse)), (("q", q), ("k", k), ("v", v)))
     o = torch.empty_like(q) if out is None else out
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
@@ -244,6 +264,7 @@ def fwd_splitkv_noalloc(q, k, v, causal: bool = False, scale: float | None = Non
     _check_buf(lse, "lse", (B, H, Nq), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _no_overlap((("out", out), ("lse", lse)), (("q", q), ("k", k), ("v", v)))
     o = torch.empty_like(q) if out is None else out
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
@@ -283,6 +304,8 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
         _check_buf(t, name, q.shape, torch.bfloat16, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _no_overlap((("dq", dq), ("dk", dk), ("dv", dv)),
+                (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do)))
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv

@@ -23,7 +23,9 @@
  *     over the keys row i attends. It may be NULL to skip its store.
  *   - Causal (causal != 0): query i attends key j only when j <= i.
  *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
- *     aligned. The library never frees or keeps them.
+ *     aligned. The library never frees or keeps them. Outputs must not
+ *     overlap the inputs or each other: the kernels read inputs while other
+ *     workgroups write outputs (not checked here; the Python binding checks).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream)
  *     of the calling thread's current device, which also holds the tensors.
  *     Calls only enqueue work and return; the caller keeps buffers alive

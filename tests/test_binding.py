@@ -1,6 +1,7 @@
 """The Python binding refuses caller-provided outputs and side inputs that do
 not match what the kernels read or write (shape, dtype, contiguity, device),
-before any launch. Small tensors; nothing is computed."""
+and outputs that share memory with an input or another output, before any
+launch. Small tensors; nothing is computed."""
 from __future__ import annotations
 
 import pytest
@@ -34,6 +35,22 @@ def test_wrong_buffers_are_refused(lib):
     for name in ("dq", "dk", "dv"):
         with pytest.raises(ValueError):
             lib.bwd(q, k, v, o, lse, o, **{name: bad_o[0]})
+
+    # outputs that share memory with an input or with another output
+    for t in (q, k, v):
+        with pytest.raises(ValueError, match="overlaps"):
+            lib.fwd(q, k, v, out=t)
+        with pytest.raises(ValueError, match="overlaps"):
+            lib.fwd_splitkv(q, k, v, out=t)
+    out = torch.empty_like(q)
+    lse_in_out = out.view(torch.float32).view(-1)[: B * H * N].view(B, H, N)
+    with pytest.raises(ValueError, match="overlaps"):
+        lib.fwd(q, k, v, out=out, lse=lse_in_out)
+    buf = torch.zeros(B, H, N, d, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError, match="overlaps"):
+        lib.bwd(q, k, v, o, lse, o, dq=o)
+    with pytest.raises(ValueError, match="overlaps"):
+        lib.bwd(q, k, v, o, lse, o, dk=buf, dv=buf)
 
     nblk = (N + 127) // 128
     with pytest.raises(ValueError):
