@@ -142,3 +142,52 @@ def test_graph_capture_bf16_forward(lib):
         torch.cuda.synchronize()
         assert torch.equal(o_graph.view(torch.int16), o_eager.view(torch.int16))
         assert torch.equal(lse_graph, lse_eager)
+
+
+@pytest.mark.parametrize("shape", [(4, 16, 1, 4096, 128, True, 0), (1, 2, 1536, 1536, 64, True, 3)],
+                         ids=["decode", "self-attention-split"])
+def test_graph_capture_splitkv_noalloc(lib, shape):
+    """The allocation-free split-KV entry (its scratch a fixed device array:
+    nothing is allocated or cleared inside the call) captured in a HIP graph:
+    every replay, with new inputs copied in and eager work between replays,
+    equals an eager fa_fwd_splitkv call bit for bit. Decode runs the split
+    kernel and the merge; Nq = Nk runs the forward kernel's split mode and
+    the merge."""
+    import torch
+    import fa_inputs
+    B, H, Nq, Nk, d, causal, splits = shape
+    q = torch.empty(B, H, Nq, d, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty(B, H, Nk, d, dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, Nq, dtype=torch.float32, device="cuda")
+
+    def load(seed):
+        gk = fa_inputs.make_qkv(B, H, Nk, d, seed)
+        gq = fa_inputs.make_qkv(B, H, Nq, d, seed + 50000)
+        for dst, bits in ((q, gq.q_bits), (k, gk.k_bits), (v, gk.v_bits)):
+            dst.copy_(fa_inputs.to_torch_bf16(bits, "cuda"))
+
+    def call():
+        lib.fwd_splitkv_noalloc(q, k, v, causal=causal, num_splits=splits, out=o, lse=lse)
+
+    load(780)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for seed in (781, 782, 783):
+        load(seed)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_graph, lse_graph = o.clone(), lse.clone()
+        o_eager, lse_eager = lib.fwd_splitkv(q, k, v, causal=causal, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o_graph.view(torch.int16), o_eager.view(torch.int16))
+        assert torch.equal(lse_graph, lse_eager)
