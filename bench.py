@@ -397,16 +397,23 @@ def main():
     warm_s = settle(step, args.warmup)
     # timed: exactly --steps steps, bracketed by synchronisations; the events
     # sit on torch's current stream, which is the stream the library launches on
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Events also split the timed steps into (up to) five equal trials, whose
+    # per-step means give the spread; they add no synchronisation.
+    n_tr = min(5, args.steps)
+    bounds = [round(i * args.steps / n_tr) for i in range(n_tr + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_tr + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
+    evs[0].record()
+    for tr in range(n_tr):
+        for _ in range(bounds[tr + 1] - bounds[tr]):
+            step()
+        evs[tr + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    kernel_ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    trial_ms = [evs[i].elapsed_time(evs[i + 1]) / (bounds[i + 1] - bounds[i])
+                for i in range(n_tr) if bounds[i + 1] > bounds[i]]
     ms_per_step = wall * 1e3 / args.steps
     f = flops(B, H, N, d, causal)
     value = f / (ms_per_step * 1e-3) / 1e12
@@ -433,7 +440,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
                      "traffic": traffic_record(), "kernel": "fwd_bf16_kernel<128,false,4>",
-                     "kernel_ms": round(kernel_ms, 5)},
+                     "kernel_ms": round(kernel_ms, 5),
+                     "kernel_ms_trials": [round(x, 5) for x in trial_ms],
+                     "kernel_ms_median": round(sorted(trial_ms)[len(trial_ms) // 2], 5)},
     }
     del q, k, v, o, lse
     fp8_extra = []
